@@ -1,0 +1,94 @@
+/*
+ * h3x_kernels.h -- kernel-level entry points of libh3x: one step of the block or the sampler
+ * per call, for per-kernel parity tests and per-kernel timing. Same conventions as h3x.h
+ * (device pointers named "dev", caller-owned buffers, asynchronous on `stream`, validation
+ * before any launch, status codes, no allocation).
+ *
+ * Internal attention layouts used by these entry points, for a sequence of N tokens and
+ * Npad = N rounded up to a multiple of 256:
+ *   q, k : dev [Npad x d] act type, head-major columns (head h = columns h*Dh .. h*Dh+Dh-1);
+ *   vt   : dev [d x Npad] act type, the value matrix transposed (row h*Dh + j, column token).
+ * Rows (columns of vt) N .. Npad-1 are written as zeros by h3x_qkv_project.
+ */
+#ifndef H3X_KERNELS_H
+#define H3X_KERNELS_H
+
+#include "h3x.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* y = x / sqrt(mean(x^2) + eps) * (1 + scale) + shift, per row of x (dev [n_rows x d], act
+ * type) into y (dev, same shape and type). shift, scale: dev [d] float32. Modulated RMSNorm is a
+ * reading: the pages only speak of a normalised MLP input (siami.tw, "3. 記憶體策略…"). */
+h3x_status h3x_norm_mod(const h3x_block_cfg *cfg, int64_t n_rows, const void *x,
+                        const float *shift, const float *scale, void *y, void *stream);
+
+/* The per-geometry 3D RoPE cos/sin table that h3x_qkv_project reads (dev float32 pairs,
+ * h3x_rope_table_bytes bytes). Built once per geometry and reused by every block. */
+size_t h3x_rope_table_bytes(const h3x_block_cfg *cfg, const h3x_geom *geom);
+h3x_status h3x_rope_table(const h3x_block_cfg *cfg, const h3x_geom *geom, void *table,
+                          void *stream);
+
+/* QKV projection of y (dev [N x d]) with packed W_qkv (and int8 scales for I8 configs, else
+ * NULL), 3D RoPE on the q and k of video rows, written to q, k, vt in the layouts above. */
+h3x_status h3x_qkv_project(const h3x_block_cfg *cfg, const h3x_geom *geom, const void *y,
+                           const void *w_qkv, const void *s_qkv, const void *rope_table,
+                           void *q, void *k, void *vt, void *stream);
+
+/* o (dev [N x d] act type) = per-head softmax(q k^T / sqrt(Dh)) v over all N keys. */
+h3x_status h3x_attention(const h3x_block_cfg *cfg, int64_t n_tokens, const void *q,
+                         const void *k, const void *vt, void *o, void *stream);
+
+/* x (dev [M x d] act type, in place) += gate (dev [d] float32) * (a @ W^T), for kind H3X_W_OUT
+ * (a: [M x d]) or H3X_W_DOWN (a: [M x F]); w packed, s its int8 scales or NULL. */
+h3x_status h3x_linear_residual(const h3x_block_cfg *cfg, int32_t kind, int64_t m, const void *a,
+                               const void *w, const void *s, const float *gate, void *x,
+                               void *stream);
+
+/* h (dev [M x F] act type) = silu(y2 @ W_gate^T) * (y2 @ W_up^T) with the packed gate/up
+ * weight (and int8 scales or NULL). */
+h3x_status h3x_linear_swiglu(const h3x_block_cfg *cfg, int64_t m, const void *y2,
+                             const void *w_gate_up, const void *s_gate_up, void *h,
+                             void *stream);
+
+/* out (dev [M x packed_rows] float32) = a @ W_packed^T (times the int8 scales): the plain
+ * product, in packed column order, for checking the contraction alone. */
+h3x_status h3x_linear_f32out(const h3x_block_cfg *cfg, int32_t kind, int64_t m, const void *a,
+                             const void *w, const void *s, float *out, void *stream);
+
+/* Token reduction (jdon.com, "330亿参数是什么概念"; siami.tw control table, row
+ * "Token 縮減"). geom is the unmerged geometry. merge: x [N x d] -> xm [N' x d], video pair
+ * (2p, 2p+1) -> row p = their mean rounded once to the act type; audio and text rows copied.
+ * unmerge: xm [N' x d] -> x [N x d], merged row p written to rows 2p and 2p+1. */
+h3x_status h3x_token_merge(const h3x_block_cfg *cfg, const h3x_geom *geom, const void *x,
+                           void *xm, void *stream);
+h3x_status h3x_token_unmerge(const h3x_block_cfg *cfg, const h3x_geom *geom, const void *xm,
+                             void *x, void *stream);
+
+/* Euler step on n_rows x d elements: z (dev float32, in place) <- float32(z + (sigma_next -
+ * sigma) * v), rounded once; v dev act type. If v_copy is not NULL, v is also copied there
+ * (the fresh-step velocity cache write). */
+h3x_status h3x_euler(const h3x_block_cfg *cfg, int64_t n_rows, float *z, const void *v,
+                     float sigma, float sigma_next, void *v_copy, void *stream);
+
+/* Plain device copy of `bytes` bytes (multiple of 16, 16-byte aligned pointers); used to
+ * calibrate hardware byte counters against a transfer of known size. */
+h3x_status h3x_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* Per-kernel timing. While enabled, every launch made by the library is bracketed by HIP
+ * events on its stream. h3x_profile_end waits for the recorded events, writes at most
+ * max_entries per-kernel totals and returns the number written (or -1 on error). */
+typedef struct {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} h3x_kernel_time;
+h3x_status h3x_profile_begin(void);
+int32_t h3x_profile_end(h3x_kernel_time *out, int32_t max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* H3X_KERNELS_H */

@@ -1,0 +1,151 @@
+"""Block- and step-level parity of the HIP path against the oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import dit, sampler
+from _util import (binding_cfg, binding_geom, host, modulation, oracle_geom, packed_block, rel_l2,
+                   to_dev)
+from test_gpu_kernels import SMALL, SMALL_F32, SMALL_I8
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2, "i8": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def B():
+    from video_diffusion_transformer_02_amd import binding
+    binding.lib()
+    return binding
+
+
+def _tol(wl):
+    return TOL["i8"] if wl.weight == "i8" else TOL[wl.act]
+
+
+def run_block(B, wl, x, b=0, merged=False, mod=None, poison=False):
+    cfg, g = binding_cfg(wl), binding_geom(wl, merged)
+    w64, pb = packed_block(wl, b)
+    m64, mdev = modulation(wl, 0, b) if mod is None else (mod, torch.from_numpy(mod.astype(np.float32)).cuda())
+    ws = B.alloc_workspace(B.block_workspace_bytes(cfg, g))
+    if poison:
+        ws.fill_(0xFF)  # every float32 / bfloat16 in it reads as NaN
+    xd = to_dev(x, wl.act)
+    B.dit_block_forward(cfg, g, pb, mdev, xd, ws)
+    torch.cuda.synchronize()
+    return xd, w64, m64
+
+
+@pytest.mark.parametrize("wl", [synth.TINY, synth.TINY_SHARP, SMALL, SMALL_F32, SMALL_I8],
+                         ids=lambda w: w.name)
+@pytest.mark.parametrize("merged", [False, True])
+def test_block_all_rows(B, wl, merged):
+    og = oracle_geom(wl, merged)
+    x = synth.storage_values(synth.normal(wl.seed_base, 77, (og.n_tokens, wl.d_model)), wl.act)
+    xd, w64, m64 = run_block(B, wl, x, merged=merged)
+    ref = dit.block_forward(x, w64, m64, og, wl.n_heads)
+    got = host(xd)
+    assert rel_l2(got, ref) < _tol(wl)
+    # The residual branch alone (x2 - x), which the residual does not dilute.
+    assert rel_l2(got - x, ref - x) < 3 * _tol(wl)
+
+
+def test_block_zero_gates_is_identity_bit_exact(B):
+    wl = SMALL
+    og = oracle_geom(wl)
+    x = synth.storage_values(synth.normal(3, 1, (og.n_tokens, wl.d_model)), "bf16")
+    mod = synth.modulation(wl, 0, 0).astype(np.float64)
+    mod[2] = 0.0
+    mod[5] = 0.0
+    xd, _, _ = run_block(B, wl, x, mod=mod)
+    np.testing.assert_array_equal(host(xd), x)
+
+
+def test_block_deterministic_and_poisoned_workspace(B):
+    wl = SMALL
+    og = oracle_geom(wl)
+    x = synth.storage_values(synth.normal(3, 2, (og.n_tokens, wl.d_model)), "bf16")
+    a, _, _ = run_block(B, wl, x)
+    b, _, _ = run_block(B, wl, x, poison=True)
+    assert torch.equal(a, b)
+
+
+def test_block_full_size_sampled_rows(B):
+    """One block at the 6 x 32 x 32 + 256 + 512 token, d = 6144 shape: 64 sampled rows."""
+    wl = synth.BLOCK
+    og = oracle_geom(wl)
+    x = synth.storage_values(synth.block_input(wl), "bf16")
+    xd, w64, m64 = run_block(B, wl, x)
+    rows = synth.sample_rows(wl)
+    ref = dit.block_forward(x, w64, m64, og, wl.n_heads, rows=rows)
+    got = host(xd)[rows]
+    assert rel_l2(got, ref) < TOL["bf16"]
+    assert rel_l2(got - x[rows], ref - x[rows]) < 3 * TOL["bf16"]
+
+
+# ---------------------------------------------------------------- sampler steps
+def _chain(B, wl, n_blocks, n_steps, reuse, tr=(-1, -1), check_every=True):
+    """Run the whole schedule on the GPU and the oracle side by side; return per-step errors."""
+    wl = wl.replace(n_blocks=n_blocks, n_steps=n_steps, reuse=reuse, tr_first=tr[0], tr_last=tr[1])
+    cfg, g = binding_cfg(wl), binding_geom(wl)
+    og = oracle_geom(wl)
+    blocks64, packed = zip(*(packed_block(wl, b) for b in range(n_blocks)))
+    arr = B.block_array(packed)
+    z0 = synth.initial_state(wl)
+    c = synth.storage_values(synth.text_rows(wl), wl.act)
+    zd = torch.from_numpy(z0.copy()).cuda()
+    cd = to_dev(c, wl.act)
+    vd = torch.zeros(wl.n_state, wl.d_model, dtype=cfg.act_dtype, device="cuda")
+    ws = B.alloc_workspace(B.step_workspace_bytes(cfg, g))
+    sig = sampler.sigma_grid(n_steps)
+    z, vref = z0.copy(), None
+    errs = []
+    for i in range(n_steps):
+        mods = [synth.modulation(wl, i, b) for b in range(n_blocks)]
+        mdev = torch.from_numpy(np.stack(mods)).cuda()
+        B.denoise_step(cfg, g, i, n_steps, reuse, float(sig[i]), float(sig[i + 1]), arr, mdev, zd, cd, vd, ws,
+                       tr[0], tr[1])
+        torch.cuda.synchronize()
+        z_prev = z
+        z, vref = sampler.denoise_step(z, c, vref, blocks64, mods, og, wl.n_heads, wl.act, i, n_steps, reuse,
+                                       sig[i], sig[i + 1], tr[0], tr[1])
+        zg = zd.cpu().numpy().astype(np.float64)
+        errs.append((rel_l2(zg, z), rel_l2(zg - z_prev, z.astype(np.float64) - z_prev)))
+        # Continue both chains from the oracle's state so that each step is checked on its own.
+        zd.copy_(torch.from_numpy(z))
+        if B.step_is_fresh(i, n_steps, reuse):
+            vd.copy_(synth.to_storage(vref, wl.act).cuda())
+    return errs
+
+
+@pytest.mark.parametrize("wl", [synth.TINY, SMALL, SMALL_I8], ids=lambda w: w.name)
+def test_denoise_chain_reuse(B, wl):
+    n_steps, reuse = (20, 2) if wl.act == "f32" else (4, 2)
+    errs = _chain(B, wl, 2, n_steps, reuse)
+    for i, (e_z, e_dz) in enumerate(errs):
+        assert e_z < _tol(wl), (i, e_z)
+        assert e_dz < 3 * _tol(wl), (i, e_dz)
+
+
+@pytest.mark.parametrize("wl", [SMALL, SMALL_F32], ids=lambda w: w.name)
+def test_denoise_chain_token_reduction(B, wl):
+    errs = _chain(B, wl, 4, 3, 1, tr=(1, 2))
+    for i, (e_z, e_dz) in enumerate(errs):
+        assert e_z < _tol(wl), (i, e_z)
+        assert e_dz < 3 * _tol(wl), (i, e_dz)
+
+
+def test_denoise_reused_step_reads_cache_only(B):
+    wl = SMALL
+    cfg, g = binding_cfg(wl), binding_geom(wl)
+    rng = np.random.default_rng(2)
+    z = rng.standard_normal((wl.n_state, wl.d_model)).astype(np.float32)
+    v = synth.storage_values(rng.standard_normal((wl.n_state, wl.d_model)).astype(np.float32), "bf16")
+    zd = torch.from_numpy(z.copy()).cuda()
+    vd = to_dev(v, "bf16")
+    B.denoise_step(cfg, g, 1, 20, 2, 0.95, 0.9, None, None, zd, None, vd, B.alloc_workspace(256))
+    torch.cuda.synchronize()
+    ref = sampler.euler_update(z, sampler.sigma_delta(0.95, 0.9), v)
+    np.testing.assert_array_equal(zd.cpu().numpy().view(np.uint32), ref.view(np.uint32))

@@ -1,0 +1,683 @@
+// C ABI of libh3x: argument validation, workspace layout, dispatch of the kernel launchers,
+// error reporting and optional per-kernel event timing. No device memory is allocated here.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "h3x.h"
+#include "h3x_kernels.h"
+#include "launch.h"
+
+using namespace h3x;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+h3x_status fail(h3x_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+// ---------------------------------------------------------------- per-kernel event timing
+struct Rec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<Rec> g_prof_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launch with events when timing is on.
+class Timed {
+ public:
+  Timed(const char* name, hipStream_t s) : name_(name), s_(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    start_ = take_event();
+    stop_ = take_event();
+    if (start_ && stop_) hipEventRecord(start_, s_);
+  }
+  ~Timed() {
+    if (!start_ || !stop_) return;
+    hipEventRecord(stop_, s_);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_recs.push_back({name_, start_, stop_});
+  }
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
+h3x_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return H3X_OK;
+  return fail(H3X_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define H3X_LAUNCH(name, stream, call)                 \
+  do {                                                 \
+    Timed _t(name, stream);                            \
+    h3x_status _st = hip_check((call), name);          \
+    if (_st != H3X_OK) return _st;                     \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+int elem_bytes(int act) { return act == H3X_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- validation
+h3x_status check_cfg(const h3x_block_cfg* c) {
+  if (!c) return fail(H3X_EINVAL, "cfg is NULL");
+  if (c->d_model <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->ffn_inner <= 0)
+    return fail(H3X_EINVAL, "cfg: sizes must be positive");
+  if (static_cast<int64_t>(c->n_heads) * c->head_dim != c->d_model)
+    return fail(H3X_EINVAL, "cfg: d_model != n_heads * head_dim");
+  if (!(c->norm_eps > 0.f) || !isfinite(c->norm_eps)) return fail(H3X_EINVAL, "cfg: norm_eps must be > 0");
+  if (!(c->rope_theta > 1.f) || !isfinite(c->rope_theta)) return fail(H3X_EINVAL, "cfg: rope_theta must be > 1");
+  if (c->act != H3X_F32 && c->act != H3X_BF16) return fail(H3X_EINVAL, "cfg: act must be F32 or BF16");
+  if (c->weight != H3X_F32 && c->weight != H3X_BF16 && c->weight != H3X_I8)
+    return fail(H3X_EINVAL, "cfg: weight must be F32, BF16 or I8");
+  if (c->act == H3X_F32) {
+    if (c->weight != H3X_F32) return fail(H3X_ENOTSUP, "cfg: F32 activations need F32 weights");
+    if (c->head_dim != 64 && c->head_dim != 128) return fail(H3X_ENOTSUP, "cfg: F32 path supports head_dim 64 or 128");
+    if (c->d_model % 64 || c->ffn_inner % 64) return fail(H3X_ENOTSUP, "cfg: F32 path needs d_model, ffn_inner % 64 == 0");
+  } else {
+    if (c->weight == H3X_F32) return fail(H3X_ENOTSUP, "cfg: BF16 activations need BF16 or I8 weights");
+    if (c->head_dim != 128) return fail(H3X_ENOTSUP, "cfg: BF16 path supports head_dim 128");
+    if (c->d_model % 256 || c->ffn_inner % 128)
+      return fail(H3X_ENOTSUP, "cfg: BF16 path needs d_model % 256 == 0 and ffn_inner % 128 == 0");
+  }
+  return H3X_OK;
+}
+
+h3x_status check_geom(const h3x_geom* g) {
+  if (!g) return fail(H3X_EINVAL, "geom is NULL");
+  if (g->frames < 0 || g->grid_h < 0 || g->grid_w < 0 || g->n_audio < 0 || g->n_text < 0)
+    return fail(H3X_EINVAL, "geom: negative size");
+  if (g->merged != 0 && g->merged != 1) return fail(H3X_EINVAL, "geom: merged must be 0 or 1");
+  if (g->merged && (g->grid_w % 2)) return fail(H3X_EINVAL, "geom: merged geometry needs an even grid_w");
+  const int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h * g->grid_w;
+  const int64_t n = (g->merged ? nv / 2 : nv) + g->n_audio + g->n_text;
+  if (n <= 0) return fail(H3X_EINVAL, "geom: no tokens");
+  if (n > (int64_t(1) << 26)) return fail(H3X_EINVAL, "geom: too many tokens");
+  return H3X_OK;
+}
+
+int64_t geom_tokens(const h3x_geom* g) {
+  const int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h * g->grid_w;
+  return (g->merged ? nv / 2 : nv) + g->n_audio + g->n_text;
+}
+
+void weight_shape(const h3x_block_cfg* c, int kind, int64_t* rows, int64_t* cols) {
+  const int64_t d = c->d_model, f = c->ffn_inner;
+  switch (kind) {
+    case H3X_W_QKV: *rows = 3 * d; *cols = d; break;
+    case H3X_W_OUT: *rows = d; *cols = d; break;
+    case H3X_W_GATE_UP: *rows = 2 * f; *cols = d; break;
+    case H3X_W_DOWN: *rows = d; *cols = f; break;
+    default: *rows = -1; *cols = -1;
+  }
+}
+
+// ---------------------------------------------------------------- workspace layout
+size_t rope_entries(const h3x_block_cfg* c, const h3x_geom* g) {
+  const int64_t kt = c->head_dim / 8, ky = 3 * c->head_dim / 16;
+  return static_cast<size_t>(g->frames * kt + g->grid_h * ky + 2 * g->grid_w * ky);
+}
+size_t rope_bytes(const h3x_block_cfg* c, const h3x_geom* g) {
+  const int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h * g->grid_w / (g->merged ? 2 : 1);
+  return align256(rope_entries(c, g) * 8) + align256(static_cast<size_t>(nv) * 16);
+}
+
+struct BlockWs {
+  int64_t n, n_pad;
+  uint8_t* y;      // [n_pad x d]
+  uint8_t* q;      // [n_pad x d]
+  uint8_t* k;      // [n_pad x d]
+  uint8_t* vt;     // [d x n_pad]
+  uint8_t* o;      // [n_pad x d]
+  uint8_t* h;      // [n_pad x F], aliases q, k, vt, o (dead once h is produced)
+  uint8_t* rope;   // rope table of the geometry
+  size_t bytes;
+};
+
+// Activation arenas by lifetime: R2 holds y (norm before attention), then y2 (norm before the
+// MLP); R1 holds q, k, v^T and the attention output o, then the SwiGLU hidden h.
+BlockWs block_layout(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* base) {
+  BlockWs w;
+  w.n = geom_tokens(g);
+  w.n_pad = round_up(w.n, 256);
+  const size_t es = elem_bytes(c->act);
+  const size_t nd = static_cast<size_t>(w.n_pad) * c->d_model * es;
+  const size_t r1 = static_cast<size_t>(w.n_pad) * es *
+                    static_cast<size_t>(c->ffn_inner > 4 * c->d_model ? c->ffn_inner : 4 * c->d_model);
+  size_t off = 0;
+  w.y = base + off; off = align256(off + nd);
+  w.q = base + off; w.k = w.q + nd; w.vt = w.k + nd; w.o = w.vt + nd; w.h = w.q;
+  off = align256(off + r1);
+  w.rope = base + off; off += rope_bytes(c, g);
+  w.bytes = off;
+  return w;
+}
+
+RopeDev rope_dev(const h3x_block_cfg* c, const h3x_geom* g, const uint8_t* rope) {
+  RopeDev r;
+  r.table = reinterpret_cast<const float2*>(rope);
+  r.rowbase = reinterpret_cast<const int4*>(rope + align256(rope_entries(c, g) * 8));
+  r.head_dim = c->head_dim;
+  r.kt = c->head_dim / 8;
+  r.ky = 3 * c->head_dim / 16;
+  r.off_y = g->frames * r.kt;
+  r.off_x = r.off_y + g->grid_h * r.ky;
+  return r;
+}
+
+h3x_status build_rope(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* rope, hipStream_t s) {
+  const RopeDev r = rope_dev(c, g, rope);
+  H3X_LAUNCH("rope_table", s,
+             launch_rope_table(geom_dev(*g), c->head_dim, c->rope_theta,
+                               reinterpret_cast<float2*>(rope), const_cast<int4*>(r.rowbase), s));
+  return H3X_OK;
+}
+
+h3x_status check_weights(const h3x_block_cfg* c, const h3x_block_weights* w) {
+  if (!w) return fail(H3X_EINVAL, "weights is NULL");
+  const void* p[4] = {w->qkv, w->out, w->gate_up, w->down};
+  const void* sc[4] = {w->s_qkv, w->s_out, w->s_gate_up, w->s_down};
+  for (int i = 0; i < 4; ++i) {
+    if (!p[i] || !aligned16(p[i])) return fail(H3X_EINVAL, "weights: NULL or misaligned weight pointer");
+    if (c->weight == H3X_I8 && !sc[i]) return fail(H3X_EINVAL, "weights: int8 weights need scales");
+    if (c->weight != H3X_I8 && sc[i]) return fail(H3X_EINVAL, "weights: scales given for non-int8 weights");
+  }
+  return H3X_OK;
+}
+
+const char* gemm_name(int epi) {
+  switch (epi) {
+    case EPI_QKV: return "gemm_qkv_rope";
+    case EPI_RESID: return "gemm_resid";
+    case EPI_SWIGLU: return "gemm_gate_up_swiglu";
+    default: return "gemm_f32out";
+  }
+}
+
+GemmArgs gemm_args(const h3x_block_cfg* c, int kind, int64_t m, const void* a, const void* w,
+                   const void* s) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  int64_t rows, cols;
+  weight_shape(c, kind, &rows, &cols);
+  g.a = a; g.w = w; g.wscale = static_cast<const uint16_t*>(s);
+  g.m = m; g.n = rows; g.k = cols;
+  g.m_pad = round_up(m, 256);
+  g.d_model = c->d_model;
+  return g;
+}
+
+// One block on prepared workspace and rope table (no validation).
+h3x_status block_forward_impl(const h3x_block_cfg* c, const h3x_geom* g, const h3x_block_weights* w,
+                              const float* mod, void* x, const BlockWs& ws, hipStream_t s) {
+  const int64_t n = ws.n, d = c->d_model;
+  const GeomDev gd = geom_dev(*g);
+  const RopeDev rd = rope_dev(c, g, ws.rope);
+  const float *shift1 = mod, *scale1 = mod + d, *gate1 = mod + 2 * d;
+  const float *shift2 = mod + 3 * d, *scale2 = mod + 4 * d, *gate2 = mod + 5 * d;
+
+  H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n, c->d_model, c->norm_eps, x, shift1, scale1, ws.y, s));
+
+  GemmArgs qa = gemm_args(c, H3X_W_QKV, n, ws.y, w->qkv, w->s_qkv);
+  qa.m_pad = ws.n_pad;
+  qa.q = ws.q; qa.kk = ws.k; qa.vt = ws.vt; qa.geom = gd; qa.rope = rd;
+  H3X_LAUNCH(gemm_name(EPI_QKV), s, launch_gemm(c->act, c->weight, EPI_QKV, qa, s));
+
+  H3X_LAUNCH("attention", s, launch_attention(c->act, n, ws.n_pad, c->n_heads, c->head_dim, ws.q, ws.k, ws.vt, ws.o, s));
+
+  GemmArgs oa = gemm_args(c, H3X_W_OUT, n, ws.o, w->out, w->s_out);
+  oa.x = x; oa.gate = gate1;
+  H3X_LAUNCH("gemm_out_resid", s, launch_gemm(c->act, c->weight, EPI_RESID, oa, s));
+
+  H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n, c->d_model, c->norm_eps, x, shift2, scale2, ws.y, s));
+
+  GemmArgs ga = gemm_args(c, H3X_W_GATE_UP, n, ws.y, w->gate_up, w->s_gate_up);
+  ga.h = ws.h;
+  H3X_LAUNCH(gemm_name(EPI_SWIGLU), s, launch_gemm(c->act, c->weight, EPI_SWIGLU, ga, s));
+
+  GemmArgs da = gemm_args(c, H3X_W_DOWN, n, ws.h, w->down, w->s_down);
+  da.x = x; da.gate = gate2;
+  H3X_LAUNCH("gemm_down_resid", s, launch_gemm(c->act, c->weight, EPI_RESID, da, s));
+  return H3X_OK;
+}
+
+struct StepWs {
+  BlockWs blk;       // sized for the unmerged geometry
+  uint8_t* x;        // [N x d] DiT activations
+  uint8_t* xm;       // [N' x d] merged activations
+  uint8_t* rope_m;   // rope table of the merged geometry
+  size_t bytes;
+};
+
+StepWs step_layout(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* base) {
+  StepWs w;
+  w.blk = block_layout(c, g, base);
+  size_t off = align256(w.blk.bytes);
+  const size_t es = elem_bytes(c->act);
+  const int64_t n = geom_tokens(g);
+  w.x = base + off; off = align256(off + static_cast<size_t>(n) * c->d_model * es);
+  h3x_geom gm = *g;
+  gm.merged = 1;
+  const int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h * g->grid_w;
+  const int64_t nm = nv / 2 + g->n_audio + g->n_text;
+  w.xm = base + off; off = align256(off + static_cast<size_t>(nm) * c->d_model * es);
+  w.rope_m = base + off; off += rope_bytes(c, &gm);
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+// ====================================================================== exported entry points
+extern "C" {
+
+int32_t h3x_abi_version(void) { return H3X_ABI_VERSION; }
+
+const char* h3x_status_string(h3x_status s) {
+  switch (s) {
+    case H3X_OK: return "ok";
+    case H3X_EINVAL: return "invalid argument";
+    case H3X_ENOTSUP: return "unsupported shape or type";
+    case H3X_EWORKSPACE: return "workspace too small";
+    case H3X_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* h3x_last_error(void) { return g_last_error.c_str(); }
+
+int64_t h3x_geom_tokens(const h3x_geom* g) {
+  if (check_geom(g) != H3X_OK) return -1;
+  return geom_tokens(g);
+}
+
+int64_t h3x_packed_rows(const h3x_block_cfg* c, int32_t kind) {
+  if (check_cfg(c) != H3X_OK) return -1;
+  int64_t r, cc;
+  weight_shape(c, kind, &r, &cc);
+  return r;
+}
+
+size_t h3x_packed_weight_bytes(const h3x_block_cfg* c, int32_t kind) {
+  if (check_cfg(c) != H3X_OK) return 0;
+  int64_t r, cc;
+  weight_shape(c, kind, &r, &cc);
+  if (r < 0) return 0;
+  const size_t es = c->weight == H3X_I8 ? 1 : (c->weight == H3X_BF16 ? 2 : 4);
+  return static_cast<size_t>(r) * cc * es;
+}
+
+int64_t h3x_packed_scale_count(const h3x_block_cfg* c, int32_t kind) {
+  if (check_cfg(c) != H3X_OK) return -1;
+  int64_t r, cc;
+  weight_shape(c, kind, &r, &cc);
+  if (r < 0) return -1;
+  return c->weight == H3X_I8 ? r : 0;
+}
+
+h3x_status h3x_pack_weights(const h3x_block_cfg* c, int32_t kind, const void* w, void* packed,
+                            void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if (c->weight == H3X_I8) return fail(H3X_EINVAL, "pack_weights: use h3x_pack_int8_weights for I8 configs");
+  int64_t rows, cols;
+  weight_shape(c, kind, &rows, &cols);
+  if (rows < 0) return fail(H3X_EINVAL, "pack_weights: bad kind");
+  if (!w || !packed || !aligned16(w) || !aligned16(packed)) return fail(H3X_EINVAL, "pack_weights: NULL or misaligned pointer");
+  if (w == packed) return fail(H3X_EINVAL, "pack_weights: in-place packing is not supported");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("pack", s, launch_pack(c->weight, kind, rows, cols, w, packed, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_pack_int8_weights(const h3x_block_cfg* c, int32_t kind, const void* w_bf16,
+                                 void* q_packed, void* scale_bf16, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if (c->weight != H3X_I8) return fail(H3X_EINVAL, "pack_int8_weights: cfg->weight must be I8");
+  int64_t rows, cols;
+  weight_shape(c, kind, &rows, &cols);
+  if (rows < 0) return fail(H3X_EINVAL, "pack_int8_weights: bad kind");
+  if (!w_bf16 || !q_packed || !scale_bf16 || !aligned16(w_bf16) || !aligned16(q_packed))
+    return fail(H3X_EINVAL, "pack_int8_weights: NULL or misaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("pack_int8", s, launch_pack_int8(kind, rows, cols, w_bf16, static_cast<int8_t*>(q_packed),
+                                              static_cast<uint16_t*>(scale_bf16), s));
+  return H3X_OK;
+}
+
+size_t h3x_block_workspace_bytes(const h3x_block_cfg* c, const h3x_geom* g) {
+  if (check_cfg(c) != H3X_OK || check_geom(g) != H3X_OK) return 0;
+  return block_layout(c, g, nullptr).bytes;
+}
+
+h3x_status h3x_dit_block_forward(const h3x_block_cfg* c, const h3x_geom* g, const h3x_block_weights* w,
+                                 const float* mod, void* x, void* ws, size_t ws_bytes, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if ((st = check_geom(g)) != H3X_OK) return st;
+  if ((st = check_weights(c, w)) != H3X_OK) return st;
+  if (!mod || !x || !ws || !aligned16(mod) || !aligned16(x) || !aligned16(ws))
+    return fail(H3X_EINVAL, "block_forward: NULL or misaligned mod / x / ws");
+  const BlockWs lay = block_layout(c, g, static_cast<uint8_t*>(ws));
+  if (ws_bytes < lay.bytes)
+    return fail(H3X_EWORKSPACE, "block_forward: workspace needs " + std::to_string(lay.bytes) + " bytes");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = build_rope(c, g, lay.rope, s)) != H3X_OK) return st;
+  return block_forward_impl(c, g, w, mod, x, lay, s);
+}
+
+int32_t h3x_step_is_fresh(int32_t step, int32_t n_steps, int32_t reuse) {
+  if (n_steps < 1 || reuse < 1 || step < 0 || step >= n_steps) return -1;
+  return (step % reuse == 0 || step == n_steps - 1) ? 1 : 0;
+}
+
+size_t h3x_step_workspace_bytes(const h3x_block_cfg* c, const h3x_geom* g) {
+  if (check_cfg(c) != H3X_OK || check_geom(g) != H3X_OK || g->merged) return 0;
+  return step_layout(c, g, nullptr).bytes;
+}
+
+h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x_step* st_,
+                            float* z, const void* text, void* v_cache, void* ws, size_t ws_bytes,
+                            void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if ((st = check_geom(g)) != H3X_OK) return st;
+  if (g->merged) return fail(H3X_EINVAL, "denoise_step: geom must be unmerged");
+  if (!st_) return fail(H3X_EINVAL, "denoise_step: step is NULL");
+  const int fresh = h3x_step_is_fresh(st_->step, st_->n_steps, st_->reuse);
+  if (fresh < 0) return fail(H3X_EINVAL, "denoise_step: need 0 <= step < n_steps and reuse >= 1");
+  if (!isfinite(st_->sigma) || !isfinite(st_->sigma_next)) return fail(H3X_EINVAL, "denoise_step: non-finite sigma");
+  const int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h * g->grid_w;
+  const int64_t n_state = nv + g->n_audio;
+  if (!z || !v_cache || !aligned16(z) || !aligned16(v_cache)) return fail(H3X_EINVAL, "denoise_step: NULL or misaligned z / v_cache");
+  if (fresh) {
+    if (st_->n_blocks < 1 || !st_->blocks || !st_->mod || !aligned16(st_->mod))
+      return fail(H3X_EINVAL, "denoise_step: fresh step needs n_blocks >= 1, blocks and mod");
+    for (int b = 0; b < st_->n_blocks; ++b)
+      if ((st = check_weights(c, &st_->blocks[b])) != H3X_OK) return st;
+    const bool tr_off = st_->tr_first == -1 && st_->tr_last == -1;
+    if (!tr_off) {
+      if (st_->tr_first < 0 || st_->tr_first > st_->tr_last || st_->tr_last >= st_->n_blocks)
+        return fail(H3X_EINVAL, "denoise_step: need 0 <= tr_first <= tr_last < n_blocks (or -1, -1)");
+      if (g->grid_w % 2) return fail(H3X_EINVAL, "denoise_step: token reduction needs an even grid_w");
+    }
+    if (g->n_text > 0 && (!text || !aligned16(text))) return fail(H3X_EINVAL, "denoise_step: NULL or misaligned text");
+    if (!ws || !aligned16(ws)) return fail(H3X_EINVAL, "denoise_step: NULL or misaligned workspace");
+    const size_t need = step_layout(c, g, nullptr).bytes;
+    if (ws_bytes < need)
+      return fail(H3X_EWORKSPACE, "denoise_step: workspace needs " + std::to_string(need) + " bytes");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float delta = st_->sigma_next - st_->sigma;  // float32 subtraction
+  const int64_t n_elems = n_state * c->d_model;
+  if (!fresh) {
+    H3X_LAUNCH("euler", s, launch_euler(c->act, n_elems, z, v_cache, delta, nullptr, s));
+    return H3X_OK;
+  }
+  const StepWs lay = step_layout(c, g, static_cast<uint8_t*>(ws));
+  h3x_geom gm = *g;
+  gm.merged = 1;
+  if ((st = build_rope(c, g, lay.blk.rope, s)) != H3X_OK) return st;
+  const bool use_tr = st_->tr_first >= 0;
+  if (use_tr && (st = build_rope(c, &gm, lay.rope_m, s)) != H3X_OK) return st;
+
+  H3X_LAUNCH("assemble", s, launch_assemble(c->act, n_state, g->n_text, c->d_model, z, text, lay.x, s));
+  const size_t mod_stride = 6 * static_cast<size_t>(c->d_model);
+  bool merged = false;
+  for (int b = 0; b < st_->n_blocks; ++b) {
+    if (use_tr && b == st_->tr_first) {
+      H3X_LAUNCH("token_merge", s, launch_token_merge(c->act, geom_dev(*g), c->d_model, lay.x, lay.xm, s));
+      merged = true;
+    }
+    if (merged && b == st_->tr_last + 1) {
+      H3X_LAUNCH("token_unmerge", s, launch_token_unmerge(c->act, geom_dev(*g), c->d_model, lay.xm, lay.x, s));
+      merged = false;
+    }
+    BlockWs bw = lay.blk;
+    const h3x_geom* gb = merged ? &gm : g;
+    bw.n = geom_tokens(gb);
+    bw.n_pad = round_up(bw.n, 256);
+    // Re-derive the arena pointers for the (smaller) merged sequence inside the same memory.
+    if (merged) {
+      BlockWs m = block_layout(c, gb, lay.blk.y);
+      m.rope = lay.rope_m;
+      bw = m;
+    }
+    if ((st = block_forward_impl(c, gb, &st_->blocks[b], st_->mod + b * mod_stride,
+                                 merged ? lay.xm : lay.x, bw, s)) != H3X_OK)
+      return st;
+  }
+  if (merged)
+    H3X_LAUNCH("token_unmerge", s, launch_token_unmerge(c->act, geom_dev(*g), c->d_model, lay.xm, lay.x, s));
+  H3X_LAUNCH("euler", s, launch_euler(c->act, n_elems, z, lay.x, delta, v_cache, s));
+  return H3X_OK;
+}
+
+// ---------------------------------------------------------------- kernel-level entry points
+h3x_status h3x_norm_mod(const h3x_block_cfg* c, int64_t n_rows, const void* x, const float* shift,
+                        const float* scale, void* y, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if (n_rows < 0) return fail(H3X_EINVAL, "norm_mod: n_rows < 0");
+  if (!x || !shift || !scale || !y || !aligned16(x) || !aligned16(y) || !aligned16(shift) || !aligned16(scale))
+    return fail(H3X_EINVAL, "norm_mod: NULL or misaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n_rows, c->d_model, c->norm_eps, x, shift, scale, y, s));
+  return H3X_OK;
+}
+
+size_t h3x_rope_table_bytes(const h3x_block_cfg* c, const h3x_geom* g) {
+  if (check_cfg(c) != H3X_OK || check_geom(g) != H3X_OK) return 0;
+  return rope_bytes(c, g);
+}
+
+h3x_status h3x_rope_table(const h3x_block_cfg* c, const h3x_geom* g, void* table, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if ((st = check_geom(g)) != H3X_OK) return st;
+  if (!table || !aligned16(table)) return fail(H3X_EINVAL, "rope_table: NULL or misaligned table");
+  return build_rope(c, g, static_cast<uint8_t*>(table), static_cast<hipStream_t>(stream));
+}
+
+h3x_status h3x_qkv_project(const h3x_block_cfg* c, const h3x_geom* g, const void* y, const void* w_qkv,
+                           const void* s_qkv, const void* rope_table, void* q, void* k, void* vt,
+                           void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if ((st = check_geom(g)) != H3X_OK) return st;
+  if (!y || !w_qkv || !rope_table || !q || !k || !vt) return fail(H3X_EINVAL, "qkv_project: NULL pointer");
+  if (!aligned16(y) || !aligned16(w_qkv) || !aligned16(rope_table) || !aligned16(q) || !aligned16(k) || !aligned16(vt))
+    return fail(H3X_EINVAL, "qkv_project: misaligned pointer");
+  if ((c->weight == H3X_I8) != (s_qkv != nullptr)) return fail(H3X_EINVAL, "qkv_project: scales iff int8 weights");
+  const int64_t n = geom_tokens(g);
+  GemmArgs a = gemm_args(c, H3X_W_QKV, n, y, w_qkv, s_qkv);
+  a.q = q; a.kk = k; a.vt = vt; a.geom = geom_dev(*g);
+  a.rope = rope_dev(c, g, static_cast<const uint8_t*>(rope_table));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH(gemm_name(EPI_QKV), s, launch_gemm(c->act, c->weight, EPI_QKV, a, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_attention(const h3x_block_cfg* c, int64_t n_tokens, const void* q, const void* k,
+                         const void* vt, void* o, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if (n_tokens < 1 || n_tokens > (int64_t(1) << 26)) return fail(H3X_EINVAL, "attention: bad n_tokens");
+  if (!q || !k || !vt || !o || !aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
+    return fail(H3X_EINVAL, "attention: NULL or misaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("attention", s, launch_attention(c->act, n_tokens, round_up(n_tokens, 256), c->n_heads, c->head_dim, q, k, vt, o, s));
+  return H3X_OK;
+}
+
+static h3x_status linear_common(const h3x_block_cfg* c, int32_t kind, int64_t m, const void* a,
+                                const void* w, const void* sc) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if (kind < H3X_W_QKV || kind > H3X_W_DOWN) return fail(H3X_EINVAL, "linear: bad kind");
+  if (m < 0 || m > (int64_t(1) << 26)) return fail(H3X_EINVAL, "linear: bad m");
+  if (!a || !w || !aligned16(a) || !aligned16(w)) return fail(H3X_EINVAL, "linear: NULL or misaligned pointer");
+  if ((c->weight == H3X_I8) != (sc != nullptr)) return fail(H3X_EINVAL, "linear: scales iff int8 weights");
+  return H3X_OK;
+}
+
+h3x_status h3x_linear_residual(const h3x_block_cfg* c, int32_t kind, int64_t m, const void* a, const void* w,
+                               const void* sc, const float* gate, void* x, void* stream) {
+  h3x_status st = linear_common(c, kind, m, a, w, sc);
+  if (st != H3X_OK) return st;
+  if (kind != H3X_W_OUT && kind != H3X_W_DOWN) return fail(H3X_EINVAL, "linear_residual: kind must be OUT or DOWN");
+  if (!gate || !x || !aligned16(x)) return fail(H3X_EINVAL, "linear_residual: NULL or misaligned gate / x");
+  GemmArgs g = gemm_args(c, kind, m, a, w, sc);
+  g.x = x; g.gate = gate;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH(kind == H3X_W_OUT ? "gemm_out_resid" : "gemm_down_resid", s, launch_gemm(c->act, c->weight, EPI_RESID, g, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_linear_swiglu(const h3x_block_cfg* c, int64_t m, const void* y2, const void* w, const void* sc,
+                             void* h, void* stream) {
+  h3x_status st = linear_common(c, H3X_W_GATE_UP, m, y2, w, sc);
+  if (st != H3X_OK) return st;
+  if (!h || !aligned16(h)) return fail(H3X_EINVAL, "linear_swiglu: NULL or misaligned h");
+  GemmArgs g = gemm_args(c, H3X_W_GATE_UP, m, y2, w, sc);
+  g.h = h;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH(gemm_name(EPI_SWIGLU), s, launch_gemm(c->act, c->weight, EPI_SWIGLU, g, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_linear_f32out(const h3x_block_cfg* c, int32_t kind, int64_t m, const void* a, const void* w,
+                             const void* sc, float* out, void* stream) {
+  h3x_status st = linear_common(c, kind, m, a, w, sc);
+  if (st != H3X_OK) return st;
+  if (!out || !aligned16(out)) return fail(H3X_EINVAL, "linear_f32out: NULL or misaligned out");
+  GemmArgs g = gemm_args(c, kind, m, a, w, sc);
+  g.out = out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH(gemm_name(EPI_F32), s, launch_gemm(c->act, c->weight, EPI_F32, g, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_token_merge(const h3x_block_cfg* c, const h3x_geom* g, const void* x, void* xm, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if ((st = check_geom(g)) != H3X_OK) return st;
+  if (g->merged || g->grid_w % 2) return fail(H3X_EINVAL, "token_merge: need an unmerged geometry with even grid_w");
+  if (!x || !xm || !aligned16(x) || !aligned16(xm) || x == xm) return fail(H3X_EINVAL, "token_merge: bad pointers");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("token_merge", s, launch_token_merge(c->act, geom_dev(*g), c->d_model, x, xm, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_token_unmerge(const h3x_block_cfg* c, const h3x_geom* g, const void* xm, void* x, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if ((st = check_geom(g)) != H3X_OK) return st;
+  if (g->merged || g->grid_w % 2) return fail(H3X_EINVAL, "token_unmerge: need an unmerged geometry with even grid_w");
+  if (!x || !xm || !aligned16(x) || !aligned16(xm) || x == xm) return fail(H3X_EINVAL, "token_unmerge: bad pointers");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("token_unmerge", s, launch_token_unmerge(c->act, geom_dev(*g), c->d_model, xm, x, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_euler(const h3x_block_cfg* c, int64_t n_rows, float* z, const void* v, float sigma,
+                     float sigma_next, void* v_copy, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if (n_rows < 0) return fail(H3X_EINVAL, "euler: n_rows < 0");
+  if (!isfinite(sigma) || !isfinite(sigma_next)) return fail(H3X_EINVAL, "euler: non-finite sigma");
+  if (!z || !v || !aligned16(z) || !aligned16(v) || (v_copy && !aligned16(v_copy)))
+    return fail(H3X_EINVAL, "euler: NULL or misaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("euler", s, launch_euler(c->act, n_rows * c->d_model, z, v, sigma_next - sigma, v_copy, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst || !aligned16(src) || !aligned16(dst) || (bytes & 15))
+    return fail(H3X_EINVAL, "copy: NULL / misaligned pointer or size not a multiple of 16");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("copy", s, launch_copy(src, dst, bytes, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = true;
+  return H3X_OK;
+}
+
+int32_t h3x_profile_end(h3x_kernel_time* out, int32_t max_entries) {
+  std::vector<Rec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = false;
+    recs.swap(g_prof_recs);
+  }
+  std::vector<h3x_kernel_time> agg;
+  int32_t status = 0;
+  for (const Rec& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      status = -1;
+      continue;
+    }
+    bool found = false;
+    for (auto& a : agg)
+      if (strncmp(a.name, r.name, sizeof(a.name)) == 0) {
+        a.launches += 1;
+        a.total_ms += ms;
+        found = true;
+      }
+    if (!found) {
+      h3x_kernel_time t;
+      memset(&t, 0, sizeof(t));
+      strncpy(t.name, r.name, sizeof(t.name) - 1);
+      t.launches = 1;
+      t.total_ms = ms;
+      agg.push_back(t);
+    }
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (const Rec& r : recs) {
+      g_event_pool.push_back(r.start);
+      g_event_pool.push_back(r.stop);
+    }
+  }
+  if (status < 0) {
+    g_last_error = "profile_end: event query failed";
+    return -1;
+  }
+  const int32_t n = static_cast<int32_t>(agg.size()) < max_entries ? static_cast<int32_t>(agg.size()) : max_entries;
+  for (int32_t i = 0; i < n && out; ++i) out[i] = agg[i];
+  return n;
+}
+
+}  // extern "C"

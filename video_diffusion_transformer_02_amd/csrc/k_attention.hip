@@ -1,0 +1,270 @@
+// Full bidirectional attention over the joint token sequence, softmax(q k^T / sqrt(Dh)) v per
+// head, with no mask (every token attends to every token).
+//
+//  * attn_mfma_kernel (bfloat16, Dh = 128): flash attention with online softmax. A workgroup
+//    of four waves owns 128 queries of one head (32 per wave) and walks the keys in tiles of
+//    64, double-buffered in LDS (K tile [64 x 128], V^T tile [128 x 64], 16-byte chunks
+//    XOR-swizzled by row). Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that
+//    a lane holds 32 scores of a single query: the running max needs one cross-lane exchange
+//    (lane ^ 32) per tile, the running sum none until the end. The probabilities are already
+//    in the B-operand layout of O^T += V^T P^T, so they never leave registers; V^T is read from
+//    LDS in the matching key order. Scores are scaled into base-2 exponent units once
+//    (log2(e) / sqrt(Dh)) and exponentiated with the hardware exp2.
+//  * attn_f32_kernel: float32, one thread per (query, head), online softmax over keys; the
+//    k and v reads of a wave are broadcasts (all its lanes read the same key).
+#include <math.h>
+
+#include "launch.h"
+
+namespace h3x {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kDh = 128;
+constexpr int kBQ = 128;  // queries per workgroup
+constexpr int kBK = 64;   // keys per tile
+constexpr int kTileK = kBK * kDh * 2;   // bytes of the K tile
+constexpr int kTileV = kDh * kBK * 2;   // bytes of the V^T tile
+constexpr int kStage = kTileK + kTileV;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// K tile: [64 keys][128 dims] = 16 chunks of 16 bytes per row, chunk index ^ (row & 15).
+__device__ __forceinline__ int k_off(int row, int c) { return row * 256 + ((c ^ (row & 15)) << 4); }
+// V^T tile: [128 dims][64 keys] = 8 chunks per row, chunk index ^ (row & 7).
+__device__ __forceinline__ int v_off(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+
+__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
+                                                                 const uint16_t* __restrict__ k,
+                                                                 const uint16_t* __restrict__ vt,
+                                                                 uint16_t* __restrict__ o,
+                                                                 int n, int n_pad, int n_heads,
+                                                                 int qblocks) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+
+  const int total = n_heads * qblocks;
+  const int per_xcd = gridDim.x / 8;
+  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (logical >= total) return;
+  const int head = logical / qblocks;
+  const int qb = logical % qblocks;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, hi = lane >> 5;
+  const int64_t d = static_cast<int64_t>(n_heads) * kDh;
+  const int64_t qrow = static_cast<int64_t>(qb) * kBQ + wave * 32 + li;
+
+  // Q fragments (B operand): dims 16s + 8hi .. +8 of this lane's query.
+  bf16x8 qf[8];
+  {
+    const uint16_t* qp = q + qrow * d + head * kDh + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s));
+  }
+
+  const uint16_t* kbase = k + head * kDh;
+  const uint16_t* vbase = vt + static_cast<int64_t>(head) * kDh * n_pad;
+  u32x4 rk[4], rv[4];
+  auto load_tile = [&](int kb) {
+    const int64_t key0 = static_cast<int64_t>(kb) * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 4) + 16 * i;  // key
+      rk[i] = *reinterpret_cast<const u32x4*>(kbase + (key0 + row) * d + (tid & 15) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 3) + 32 * i;  // dim
+      rv[i] = *reinterpret_cast<const u32x4*>(vbase + row * static_cast<int64_t>(n_pad) + key0 + (tid & 7) * 8);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    uint8_t* sk = smem + stage * kStage;
+    uint8_t* sv = sk + kTileK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sk + k_off((tid >> 4) + 16 * i, tid & 15)) = rk[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sv + v_off((tid >> 3) + 32 * i, tid & 7)) = rv[i];
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = 1.4426950408889634f / sqrtf(static_cast<float>(kDh));
+
+  const int ktiles = (n + kBK - 1) / kBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kb = 0; kb < ktiles; ++kb) {
+    const int stage = kb & 1;
+    if (kb + 1 < ktiles) load_tile(kb + 1);
+    const uint8_t* sk = smem + stage * kStage;
+    const uint8_t* sv = sk + kTileK;
+
+    // S^T for keys kb*64 + 32*kh + (8b + 4hi + r), query qrow.
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(sk + k_off(32 * kh + li, 2 * s + hi)));
+        sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kh], 0, 0, 0);
+      }
+    }
+
+    // Online softmax in base-2 units.
+    float mx = -INFINITY;
+    const bool tail = (kb + 1) * kBK > n;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float t = sacc[kh][e] * c;
+        if (tail) {
+          const int key = kb * kBK + 32 * kh + 8 * (e >> 2) + 4 * hi + (e & 3);
+          if (key >= n) t = -INFINITY;
+        }
+        sacc[kh][e] = t;
+        mx = fmaxf(mx, t);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(sacc[kh][e] - m_new);
+        sacc[kh][e] = pv;
+        psum += pv;
+      }
+    l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+
+    // P^T fragments: for 16-key group j, element e is key 16j + 8(e/4) + 4hi + e%4.
+    bf16x8 pf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int b = 2 * (j & 1) + (e >> 2);
+        pf[j][e] = static_cast<__bf16>(sacc[j >> 1][4 * b + (e & 3)]);
+      }
+
+    // O^T[dim][query] += V^T P^T.
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int row = 32 * db + li;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(sv + v_off(row, 2 * j) + 8 * hi);
+        const u32x2 hi2 = *reinterpret_cast<const u32x2*>(sv + v_off(row, 2 * j + 1) + 8 * hi);
+        const bf16x8 a = as_bf16x8(u32x4{lo.x, lo.y, hi2.x, hi2.y});
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[db], 0, 0, 0);
+      }
+
+    if (kb + 1 < ktiles) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l;
+  if (qrow < n) {
+    uint16_t* op = o + qrow * d + head * kDh;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int dim = 32 * db + 8 * b + 4 * hi;
+        const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(oacc[db][4 * b + 0] * inv)) |
+                            (static_cast<uint32_t>(f32_to_bf16_bits(oacc[db][4 * b + 1] * inv)) << 16);
+        const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(oacc[db][4 * b + 2] * inv)) |
+                            (static_cast<uint32_t>(f32_to_bf16_bits(oacc[db][4 * b + 3] * inv)) << 16);
+        *reinterpret_cast<u32x2*>(op + dim) = u32x2{w0, w1};
+      }
+  }
+}
+
+template <int DH>
+__global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ q,
+                                                      const float* __restrict__ k,
+                                                      const float* __restrict__ vt,
+                                                      float* __restrict__ o, int n, int n_pad,
+                                                      int n_heads) {
+  const int head = blockIdx.y;
+  const int64_t qi = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x;
+  const int64_t d = static_cast<int64_t>(n_heads) * DH;
+  const int64_t qr = qi < n ? qi : n - 1;
+  float qv[DH], acc[DH];
+  const float scale = 1.0f / sqrtf(static_cast<float>(DH));
+#pragma unroll
+  for (int c = 0; c < DH; ++c) {
+    qv[c] = q[qr * d + head * DH + c] * scale;
+    acc[c] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j < n; ++j) {
+    const float* kj = k + static_cast<int64_t>(j) * d + head * DH;
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < DH; ++c) s = fmaf(qv[c], kj[c], s);
+    const float m_new = fmaxf(m, s);
+    const float alpha = expf(m - m_new);
+    const float pj = expf(s - m_new);
+    l = fmaf(l, alpha, pj);
+    m = m_new;
+    const float* vj = vt + static_cast<int64_t>(head) * DH * n_pad + j;
+#pragma unroll
+    for (int c = 0; c < DH; ++c) acc[c] = fmaf(pj, vj[static_cast<int64_t>(c) * n_pad], acc[c] * alpha);
+  }
+  if (qi < n) {
+#pragma unroll
+    for (int c = 0; c < DH; ++c) o[qi * d + head * DH + c] = acc[c] / l;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_heads, int head_dim,
+                            const void* q, const void* k, const void* vt, void* o,
+                            hipStream_t s) {
+  if (n_tokens == 0) return hipSuccess;
+  const int n = static_cast<int>(n_tokens), np = static_cast<int>(n_pad);
+  if (act == H3X_BF16) {
+    const int qblocks = (n + kBQ - 1) / kBQ;
+    const int total = qblocks * n_heads;
+    const int grid = (total + 7) / 8 * 8;
+    attn_mfma_kernel<<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(q),
+                                               static_cast<const uint16_t*>(k),
+                                               static_cast<const uint16_t*>(vt),
+                                               static_cast<uint16_t*>(o), n, np, n_heads, qblocks);
+  } else {
+    dim3 grid(static_cast<unsigned>((n + 63) / 64), static_cast<unsigned>(n_heads));
+    if (head_dim == 64)
+      attn_f32_kernel<64><<<grid, 64, 0, s>>>(static_cast<const float*>(q),
+                                              static_cast<const float*>(k),
+                                              static_cast<const float*>(vt),
+                                              static_cast<float*>(o), n, np, n_heads);
+    else
+      attn_f32_kernel<128><<<grid, 64, 0, s>>>(static_cast<const float*>(q),
+                                               static_cast<const float*>(k),
+                                               static_cast<const float*>(vt),
+                                               static_cast<float*>(o), n, np, n_heads);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace h3x

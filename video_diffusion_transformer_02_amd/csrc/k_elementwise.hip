@@ -1,0 +1,415 @@
+// Memory-bound kernels of the hot path: modulated RMSNorm, token merge / unmerge, the Euler
+// update, assembly of the DiT input, weight packing (bf16 / f32 permutation and int8
+// quantisation), the 3D RoPE table and a plain copy. All move 16 bytes per lane per access.
+#include <math.h>
+
+#include "launch.h"
+
+namespace h3x {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <class E> struct Vec;
+template <> struct Vec<F32> { static constexpr int n = 4; };
+template <> struct Vec<BF16> { static constexpr int n = 8; };
+
+// Load / store n consecutive elements (16 bytes) as floats.
+template <class E>
+__device__ __forceinline__ void load16(const typename E::T* p, float* out) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+  if constexpr (sizeof(typename E::T) == 4) {
+    out[0] = __uint_as_float(raw.x); out[1] = __uint_as_float(raw.y);
+    out[2] = __uint_as_float(raw.z); out[3] = __uint_as_float(raw.w);
+  } else {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+template <class E>
+__device__ __forceinline__ void store16(typename E::T* p, const float* v) {
+  uint4 raw;
+  if constexpr (sizeof(typename E::T) == 4) {
+    raw.x = __float_as_uint(v[0]); raw.y = __float_as_uint(v[1]);
+    raw.z = __float_as_uint(v[2]); raw.w = __float_as_uint(v[3]);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i + 1])) << 16);
+    raw = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  *reinterpret_cast<uint4*>(p) = raw;
+}
+
+// ---------------------------------------------------------------- modulated RMSNorm
+// One workgroup per row: sum of squares in float32 (wave reduction, then across the four
+// waves through LDS), then y = x * rsqrt(ms + eps) * (1 + scale) + shift.
+template <class E>
+__global__ __launch_bounds__(kThreads) void norm_mod_kernel(const typename E::T* __restrict__ x,
+                                                            const float* __restrict__ shift,
+                                                            const float* __restrict__ scale,
+                                                            typename E::T* __restrict__ y,
+                                                            int d, float eps) {
+  constexpr int V = Vec<E>::n;
+  __shared__ float part[kThreads / 64];
+  const int64_t row = blockIdx.x;
+  const typename E::T* xr = x + row * d;
+  typename E::T* yr = y + row * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x * V; i < d; i += kThreads * V) {
+    float v[V];
+    load16<E>(xr + i, v);
+#pragma unroll
+    for (int j = 0; j < V; ++j) ss = fmaf(v[j], v[j], ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) tot += part[w];
+  const float r = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
+  for (int i = threadIdx.x * V; i < d; i += kThreads * V) {
+    float v[V];
+    load16<E>(xr + i, v);
+    const float4* sc4 = reinterpret_cast<const float4*>(scale + i);
+    const float4* sh4 = reinterpret_cast<const float4*>(shift + i);
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) {
+      const float4 sc = sc4[j], sh = sh4[j];
+      v[4 * j + 0] = fmaf(v[4 * j + 0] * r, 1.f + sc.x, sh.x);
+      v[4 * j + 1] = fmaf(v[4 * j + 1] * r, 1.f + sc.y, sh.y);
+      v[4 * j + 2] = fmaf(v[4 * j + 2] * r, 1.f + sc.z, sh.z);
+      v[4 * j + 3] = fmaf(v[4 * j + 3] * r, 1.f + sc.w, sh.w);
+    }
+    store16<E>(yr + i, v);
+  }
+}
+
+// ---------------------------------------------------------------- token merge / unmerge
+// Merged row p < n_video/2 is the mean of unmerged rows 2p and 2p+1: their float32 sum is
+// exact (or, when it is not, too small a change to move the bfloat16 result), halving is exact,
+// so a single rounding to the storage type gives the correctly rounded mean.
+template <class E>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const typename E::T* __restrict__ x,
+                                                         typename E::T* __restrict__ xm,
+                                                         int64_t nv_half, int64_t n_out,
+                                                         int d) {
+  constexpr int V = Vec<E>::n;
+  const int64_t cpr = d / V;
+  const int64_t total = n_out * cpr;
+  for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = idx / cpr, c = (idx % cpr) * V;
+    float out[V];
+    if (row < nv_half) {
+      float a[V], b[V];
+      load16<E>(x + (2 * row) * d + c, a);
+      load16<E>(x + (2 * row + 1) * d + c, b);
+#pragma unroll
+      for (int j = 0; j < V; ++j) out[j] = (a[j] + b[j]) * 0.5f;
+    } else {
+      load16<E>(x + (row + nv_half) * d + c, out);
+    }
+    store16<E>(xm + row * d + c, out);
+  }
+}
+
+template <class E>
+__global__ __launch_bounds__(kThreads) void unmerge_kernel(const typename E::T* __restrict__ xm,
+                                                           typename E::T* __restrict__ x,
+                                                           int64_t n_video, int64_t n_out,
+                                                           int d) {
+  constexpr int V = Vec<E>::n;
+  const int64_t cpr = d / V;
+  const int64_t total = n_out * cpr;
+  for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = idx / cpr, c = (idx % cpr) * V;
+    const int64_t src = row < n_video ? row / 2 : row - n_video / 2;
+    const uint4 raw = *reinterpret_cast<const uint4*>(xm + src * d + c);
+    *reinterpret_cast<uint4*>(x + row * d + c) = raw;
+  }
+}
+
+// ---------------------------------------------------------------- Euler update
+// z <- fma(delta, v, z): one rounding of the exact z + delta * v.
+template <class E>
+__global__ __launch_bounds__(kThreads) void euler_kernel(float* __restrict__ z,
+                                                         const typename E::T* __restrict__ v,
+                                                         float delta,
+                                                         typename E::T* __restrict__ v_copy,
+                                                         int64_t n4) {
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * kThreads) {
+    float4 zz = reinterpret_cast<float4*>(z)[i];
+    float vv[4];
+    if constexpr (sizeof(typename E::T) == 4) {
+      const float4 t = reinterpret_cast<const float4*>(v)[i];
+      vv[0] = t.x; vv[1] = t.y; vv[2] = t.z; vv[3] = t.w;
+      if (v_copy) reinterpret_cast<float4*>(v_copy)[i] = t;
+    } else {
+      const uint2 t = reinterpret_cast<const uint2*>(v)[i];
+      vv[0] = __uint_as_float(t.x << 16); vv[1] = __uint_as_float(t.x & 0xffff0000u);
+      vv[2] = __uint_as_float(t.y << 16); vv[3] = __uint_as_float(t.y & 0xffff0000u);
+      if (v_copy) reinterpret_cast<uint2*>(v_copy)[i] = t;
+    }
+    zz.x = fmaf(delta, vv[0], zz.x);
+    zz.y = fmaf(delta, vv[1], zz.y);
+    zz.z = fmaf(delta, vv[2], zz.z);
+    zz.w = fmaf(delta, vv[3], zz.w);
+    reinterpret_cast<float4*>(z)[i] = zz;
+  }
+}
+
+// ---------------------------------------------------------------- DiT input [act(z); text]
+template <class E>
+__global__ __launch_bounds__(kThreads) void assemble_kernel(const float* __restrict__ z,
+                                                            const typename E::T* __restrict__ text,
+                                                            typename E::T* __restrict__ x,
+                                                            int64_t n_state, int64_t n_rows,
+                                                            int d) {
+  const int64_t cpr = d / 4;
+  const int64_t total = n_rows * cpr;
+  for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = idx / cpr, c = (idx % cpr) * 4;
+    if (row < n_state) {
+      const float4 t = *reinterpret_cast<const float4*>(z + row * d + c);
+      E::store(x, row * d + c + 0, t.x);
+      E::store(x, row * d + c + 1, t.y);
+      E::store(x, row * d + c + 2, t.z);
+      E::store(x, row * d + c + 3, t.w);
+    } else {
+      const int64_t tr = row - n_state;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[row * d + c + j] = text[tr * d + c + j];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void copy_kernel(const uint4* __restrict__ src,
+                                                        uint4* __restrict__ dst, int64_t n16) {
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads)
+    dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------- 3D RoPE table
+// Entry (axis, position, pair k) = (cos, sin) of position * theta^(-2k / D), D the chunk size,
+// evaluated in double precision and rounded to float32. The x axis is tabulated at half-unit
+// positions so that merged tokens (x = 2m + 0.5) index it directly.
+__global__ void rope_table_kernel(float2* __restrict__ table, int frames, int grid_h,
+                                  int grid_w, int kt, int ky, double log2_theta) {
+  const int n_t = frames * kt, n_y = grid_h * ky, n_x = 2 * grid_w * ky;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_t + n_y + n_x) return;
+  double pos;
+  int k, pairs;
+  if (i < n_t) {
+    pos = i / kt; k = i % kt; pairs = kt;
+  } else if (i < n_t + n_y) {
+    pos = (i - n_t) / ky; k = (i - n_t) % ky; pairs = ky;
+  } else {
+    pos = 0.5 * ((i - n_t - n_y) / ky); k = (i - n_t - n_y) % ky; pairs = ky;
+  }
+  const double omega = exp2(-2.0 * k / (2.0 * pairs) * log2_theta);
+  const double phi = pos * omega;
+  table[i] = make_float2(static_cast<float>(cos(phi)), static_cast<float>(sin(phi)));
+}
+
+// Per video row, the entry offsets of its t, y and x positions in the table above.
+__global__ void rope_rowbase_kernel(int4* __restrict__ rowbase, GeomDev g, int kt, int ky) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= g.n_video) return;
+  const int per_frame = g.grid_h * g.cols;
+  const int t = r / per_frame;
+  const int y = (r % per_frame) / g.cols;
+  const int c = r % g.cols;
+  const int x2 = g.merged ? 4 * c + 1 : 2 * c;
+  const int off_y = g.frames * kt, off_x = off_y + g.grid_h * ky;
+  rowbase[r] = make_int4(t * kt, off_y + y * ky, off_x + x2 * ky, 0);
+}
+
+// ---------------------------------------------------------------- weight packing
+template <class T>
+__global__ __launch_bounds__(kThreads) void pack_kernel(const T* __restrict__ w,
+                                                        T* __restrict__ packed, int kind,
+                                                        int64_t rows, int64_t cols) {
+  constexpr int V = 16 / sizeof(T);
+  const int64_t cpr = cols / V;
+  const int64_t total = rows * cpr;
+  for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t p = idx / cpr, c = (idx % cpr) * V;
+    const int64_t src = packed_source_row(kind, p, rows);
+    *reinterpret_cast<uint4*>(packed + p * cols + c) =
+        *reinterpret_cast<const uint4*>(w + src * cols + c);
+  }
+}
+
+// One workgroup per packed row: amax, scale = bf16(amax / 127), codes = clamp(rint(w / s)).
+__global__ __launch_bounds__(kThreads) void pack_int8_kernel(const uint16_t* __restrict__ w,
+                                                             int8_t* __restrict__ q,
+                                                             uint16_t* __restrict__ scale,
+                                                             int kind, int64_t rows,
+                                                             int64_t cols) {
+  __shared__ float part[kThreads / 64];
+  const int64_t p = blockIdx.x;
+  const int64_t src = packed_source_row(kind, p, rows);
+  const uint16_t* wr = w + src * cols;
+  float amax = 0.f;
+  for (int64_t c = threadIdx.x * 8; c < cols; c += kThreads * 8) {
+    float v[8];
+    load16<BF16>(wr + c, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) a = fmaxf(a, part[i]);
+  const uint16_t sbits = a == 0.f ? 0 : f32_to_bf16_bits(a / 127.0f);
+  const float s = bf16_bits_to_f32(sbits);
+  if (threadIdx.x == 0) scale[p] = sbits;
+  int8_t* qr = q + p * cols;
+  for (int64_t c = threadIdx.x * 8; c < cols; c += kThreads * 8) {
+    float v[8];
+    load16<BF16>(wr + c, v);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int qi = 0;
+      if (s != 0.f) qi = static_cast<int>(fminf(fmaxf(rintf(v[j] / s), -127.f), 127.f));
+      const uint32_t b = static_cast<uint32_t>(qi) & 0xffu;
+      if (j < 4) lo |= b << (8 * j); else hi |= b << (8 * (j - 4));
+    }
+    *reinterpret_cast<uint2*>(qr + c) = make_uint2(lo, hi);
+  }
+}
+
+int grid_for(int64_t work_items) {
+  int64_t g = (work_items + kThreads - 1) / kThreads;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return static_cast<int>(g);
+}
+
+}  // namespace
+
+hipError_t launch_norm_mod(int act, int64_t n_rows, int d, float eps, const void* x,
+                           const float* shift, const float* scale, void* y, hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  if (act == H3X_BF16)
+    norm_mod_kernel<BF16><<<dim3(n_rows), kThreads, 0, s>>>(
+        static_cast<const uint16_t*>(x), shift, scale, static_cast<uint16_t*>(y), d, eps);
+  else
+    norm_mod_kernel<F32><<<dim3(n_rows), kThreads, 0, s>>>(
+        static_cast<const float*>(x), shift, scale, static_cast<float*>(y), d, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_merge(int act, const GeomDev& g, int d, const void* x, void* xm,
+                              hipStream_t s) {
+  const int64_t nv_half = g.n_video / 2;
+  const int64_t n_out = nv_half + g.n_audio + g.n_text;
+  const int V = act == H3X_BF16 ? 8 : 4;
+  const int grid = grid_for(n_out * (d / V));
+  if (act == H3X_BF16)
+    merge_kernel<BF16><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(x),
+                                                 static_cast<uint16_t*>(xm), nv_half, n_out, d);
+  else
+    merge_kernel<F32><<<grid, kThreads, 0, s>>>(static_cast<const float*>(x),
+                                                static_cast<float*>(xm), nv_half, n_out, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_unmerge(int act, const GeomDev& g, int d, const void* xm, void* x,
+                                hipStream_t s) {
+  const int64_t n_out = g.n_video + g.n_audio + g.n_text;
+  const int V = act == H3X_BF16 ? 8 : 4;
+  const int grid = grid_for(n_out * (d / V));
+  if (act == H3X_BF16)
+    unmerge_kernel<BF16><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(xm),
+                                                   static_cast<uint16_t*>(x), g.n_video, n_out, d);
+  else
+    unmerge_kernel<F32><<<grid, kThreads, 0, s>>>(static_cast<const float*>(xm),
+                                                  static_cast<float*>(x), g.n_video, n_out, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_euler(int act, int64_t n_elems, float* z, const void* v, float delta,
+                        void* v_copy, hipStream_t s) {
+  const int64_t n4 = n_elems / 4;
+  if (n4 == 0) return hipSuccess;
+  const int grid = grid_for(n4);
+  if (act == H3X_BF16)
+    euler_kernel<BF16><<<grid, kThreads, 0, s>>>(z, static_cast<const uint16_t*>(v), delta,
+                                                 static_cast<uint16_t*>(v_copy), n4);
+  else
+    euler_kernel<F32><<<grid, kThreads, 0, s>>>(z, static_cast<const float*>(v), delta,
+                                                static_cast<float*>(v_copy), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_assemble(int act, int64_t n_state, int64_t n_text, int d, const float* z,
+                           const void* text, void* x, hipStream_t s) {
+  const int64_t n_rows = n_state + n_text;
+  const int grid = grid_for(n_rows * (d / 4));
+  if (act == H3X_BF16)
+    assemble_kernel<BF16><<<grid, kThreads, 0, s>>>(z, static_cast<const uint16_t*>(text),
+                                                    static_cast<uint16_t*>(x), n_state, n_rows, d);
+  else
+    assemble_kernel<F32><<<grid, kThreads, 0, s>>>(z, static_cast<const float*>(text),
+                                                   static_cast<float*>(x), n_state, n_rows, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  copy_kernel<<<grid_for(n16), kThreads, 0, s>>>(static_cast<const uint4*>(src),
+                                                 static_cast<uint4*>(dst), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const GeomDev& g, int head_dim, float theta, float2* table,
+                             int4* rowbase, hipStream_t s) {
+  const int kt = head_dim / 8, ky = 3 * head_dim / 16;
+  const int n = g.frames * kt + g.grid_h * ky + 2 * g.grid_w * ky;
+  rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(table, g.frames, g.grid_h, g.grid_w, kt, ky,
+                                                    log2(static_cast<double>(theta)));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.n_video == 0) return e;
+  rope_rowbase_kernel<<<(g.n_video + 255) / 256, 256, 0, s>>>(rowbase, g, kt, ky);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(int wdtype, int kind, int64_t rows, int64_t cols, const void* w,
+                       void* packed, hipStream_t s) {
+  if (wdtype == H3X_BF16) {
+    pack_kernel<uint16_t><<<grid_for(rows * cols / 8), kThreads, 0, s>>>(
+        static_cast<const uint16_t*>(w), static_cast<uint16_t*>(packed), kind, rows, cols);
+  } else {
+    pack_kernel<float><<<grid_for(rows * cols / 4), kThreads, 0, s>>>(
+        static_cast<const float*>(w), static_cast<float*>(packed), kind, rows, cols);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_int8(int kind, int64_t rows, int64_t cols, const void* w_bf16,
+                            int8_t* q, uint16_t* scale, hipStream_t s) {
+  pack_int8_kernel<<<dim3(rows), kThreads, 0, s>>>(static_cast<const uint16_t*>(w_bf16), q,
+                                                  scale, kind, rows, cols);
+  return hipGetLastError();
+}
+
+}  // namespace h3x

@@ -1,0 +1,433 @@
+// Projection GEMMs of the block: C = A * W^T with fused epilogues.
+//
+//  * gemm_mfma_kernel: bfloat16 activations, bfloat16 or int8 weights, float32 accumulation on
+//    the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16). 256 x 256 output tile per workgroup,
+//    K step 64, four waves in a 2 x 2 grid each owning 128 x 128 (4 x 4 MFMA blocks of 32 x 32).
+//    Operand tiles are staged through LDS (two stages, 16-byte chunks XOR-swizzled by row so
+//    that the MFMA operand reads are bank-conflict free); the next K step is fetched into
+//    registers while the current one is multiplied. int8 weights are widened to bfloat16 in
+//    registers (exact: |q| <= 127) and their per-row scale is applied in the epilogue.
+//    Workgroups are remapped so that each XCD (own L2) walks a contiguous run of a grouped
+//    tile order: consecutive tiles share weight panels and activation panels.
+//  * gemm_f32_kernel: float32 activations and weights (small configurations): 64 x 64 tiles,
+//    plain FMA, same epilogues.
+//
+// Epilogues: QKV (3D RoPE on video rows of q and k, v written transposed, pad rows zeroed),
+// gated residual (x += gate * acc), SwiGLU over the 32-row gate/up interleave, float32 store.
+#include <math.h>
+
+#include "launch.h"
+
+namespace h3x {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BM = 256, BN = 256, BK = 64;
+
+// ---------------------------------------------------------------- shared epilogue math
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Table index of the (cos, sin) entry turning pair `dh/2` of video row `row`.
+__device__ __forceinline__ int rope_index(const RopeDev& r, int64_t row, int dh) {
+  const int ct = r.head_dim / 4, cy = 3 * r.head_dim / 8;
+  const int4 base = r.rowbase[row];
+  if (dh < ct) return base.x + dh / 2;
+  if (dh < ct + cy) return base.y + (dh - ct) / 2;
+  return base.z + (dh - ct - cy) / 2;
+}
+
+// Rotated value of a pair member: v is this element, p its partner; even = first of the pair.
+__device__ __forceinline__ float rope_apply(float v, float p, float2 cs, bool even) {
+  return even ? fmaf(v, cs.x, -p * cs.y) : fmaf(p, cs.y, v * cs.x);
+}
+
+__device__ __forceinline__ float dpp_swap_adjacent(float v) {
+  // quad_perm [1, 0, 3, 2]: each lane receives its neighbour's value (lane ^ 1).
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+// ---------------------------------------------------------------- MFMA kernel
+template <bool kInt8>
+struct Smem {
+  static constexpr int kA = BM * BK * 2;                 // bytes of one A stage
+  static constexpr int kB = BN * BK * (kInt8 ? 1 : 2);   // bytes of one B stage
+  static constexpr int kTotal = 2 * (kA + kB);
+};
+
+// LDS byte offset of 16-byte chunk c (0..7) of bf16 row `row` in a [rows x 64] tile.
+__device__ __forceinline__ int swz16(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..3) of int8 row `row` in a [rows x 64] tile.
+__device__ __forceinline__ int swz8(int row, int c) {
+  return row * 64 + ((c ^ ((row >> 2) & 3)) << 4);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// 8 int8 codes (two dwords) -> 8 bfloat16 values, exact.
+__device__ __forceinline__ bf16x8 widen_i8(u32x2 v) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = i < 2 ? v.x : v.y;
+    const int sh = (i & 1) * 16;
+    const float lo = static_cast<float>(static_cast<int8_t>((w >> sh) & 0xff));
+    const float hi = static_cast<float>(static_cast<int8_t>((w >> (sh + 8)) & 0xff));
+    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+  return as_bf16x8(u32x4{o[0], o[1], o[2], o[3]});
+}
+
+template <bool kInt8, int kEpi>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int tiles_m,
+                                                                  int tiles_n, int group_m) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<kInt8>::kTotal];
+
+  // ---- tile selection: XCD-contiguous runs of a grouped (m-group, n) order
+  const int total = tiles_m * tiles_n;
+  const int per_xcd = gridDim.x / 8;
+  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (logical >= total) return;
+  const int group_size = group_m * tiles_n;
+  const int first_m = (logical / group_size) * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int in_group = logical % group_size;
+  const int tm = first_m + in_group % gm;
+  const int tn = in_group / gm;
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, hi = lane >> 5;
+  const int64_t K = p.k;
+  const int ktiles = static_cast<int>(K / BK);
+
+  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+  const uint8_t* Wb = static_cast<const uint8_t*>(p.w);
+
+  // ---- global -> register staging
+  u32x4 ra[8];
+  u32x4 rb[kInt8 ? 4 : 8];
+  auto load_tiles = [&](int kt) {
+    const int64_t k0 = static_cast<int64_t>(kt) * BK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      int64_t gr = m0 + row;
+      if (gr >= p.m) gr = p.m - 1;  // clamp: rows past the end are computed but never stored
+      ra[i] = *reinterpret_cast<const u32x4*>(A + gr * K + k0 + (tid & 7) * 8);
+    }
+    if constexpr (kInt8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (tid >> 2) + 64 * i;
+        rb[i] = *reinterpret_cast<const u32x4*>(Wb + (n0 + row) * K + k0 + (tid & 3) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = (tid >> 3) + 32 * i;
+        rb[i] = *reinterpret_cast<const u32x4*>(Wb + ((n0 + row) * K + k0 + (tid & 7) * 8) * 2);
+      }
+    }
+  };
+  auto store_tiles = [&](int stage) {
+    uint8_t* sa = smem + stage * (Smem<kInt8>::kA + Smem<kInt8>::kB);
+    uint8_t* sb = sa + Smem<kInt8>::kA;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(sa + swz16((tid >> 3) + 32 * i, tid & 7)) = ra[i];
+    if constexpr (kInt8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(sb + swz8((tid >> 2) + 64 * i, tid & 3)) = rb[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(sb + swz16((tid >> 3) + 32 * i, tid & 7)) = rb[i];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  load_tiles(0);
+  store_tiles(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < ktiles) load_tiles(kt + 1);
+    const uint8_t* sa = smem + stage * (Smem<kInt8>::kA + Smem<kInt8>::kB);
+    const uint8_t* sb = sa + Smem<kInt8>::kA;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int row = wm * 128 + mb * 32 + li;
+        af[mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + swz16(row, 2 * ks + hi)));
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int row = wn * 128 + nb * 32 + li;
+        if constexpr (kInt8) {
+          bfr[nb] = widen_i8(*reinterpret_cast<const u32x2*>(sb + swz8(row, ks) + 8 * hi));
+        } else {
+          bfr[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(sb + swz16(row, 2 * ks + hi)));
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+    }
+    if (kt + 1 < ktiles) store_tiles(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue. Element (mb, nb, 4b + r) of this lane: row m0 + wm*128 + mb*32 + 8b + 4hi + r,
+  // column n0 + wn*128 + nb*32 + li.
+  float csc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t col = n0 + wn * 128 + nb * 32 + li;
+    csc[nb] = kInt8 ? bf16_bits_to_f32(p.wscale[col]) : 1.0f;
+  }
+
+  if constexpr (kEpi == EPI_F32) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          const int64_t col = n0 + wn * 128 + nb * 32 + li;
+          if (row < p.m) p.out[row * p.n + col] = acc[mb][nb][e] * csc[nb];
+        }
+  } else if constexpr (kEpi == EPI_RESID) {
+    uint16_t* x = static_cast<uint16_t*>(p.x);
+    float g[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) g[nb] = p.gate[n0 + wn * 128 + nb * 32 + li] * csc[nb];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        if (row < p.m) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int64_t idx = row * p.n + n0 + wn * 128 + nb * 32 + li;
+            x[idx] = f32_to_bf16_bits(fmaf(g[nb], acc[mb][nb][e], bf16_bits_to_f32(x[idx])));
+          }
+        }
+      }
+  } else if constexpr (kEpi == EPI_SWIGLU) {
+    uint16_t* h = static_cast<uint16_t*>(p.h);
+    const int64_t F = p.n / 2;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        if (row < p.m) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const int64_t col = n0 + wn * 128 + pr * 64;  // multiple of 64: gate block, then up
+            const int64_t f = (col / 64) * 32 + li;
+            const float gv = acc[mb][2 * pr][e] * csc[2 * pr];
+            const float uv = acc[mb][2 * pr + 1][e] * csc[2 * pr + 1];
+            h[row * F + f] = f32_to_bf16_bits(silu(gv) * uv);
+          }
+        }
+      }
+  } else {  // EPI_QKV
+    const int64_t d = p.d_model;
+    const int region = static_cast<int>(n0 / d);  // 0 = q, 1 = k, 2 = v (d % 256 == 0)
+    if (region < 2) {
+      uint16_t* dst = static_cast<uint16_t*>(region == 0 ? p.q : p.kk);
+      const bool even = (li & 1) == 0;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int64_t f = n0 + wn * 128 + nb * 32 + li - region * d;
+        const int dh = static_cast<int>(f % p.rope.head_dim);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+            const float v = acc[mb][nb][e] * csc[nb];
+            const float partner = dpp_swap_adjacent(v);
+            float out = v;
+            if (row < p.geom.n_video) {
+              const float2 cs = p.rope.table[rope_index(p.rope, row, dh)];
+              out = rope_apply(v, partner, cs, even);
+            }
+            if (row >= p.m) out = 0.f;
+            if (row < p.m_pad) dst[row * d + f] = f32_to_bf16_bits(out);
+          }
+      }
+    } else {
+      uint16_t* vt = static_cast<uint16_t*>(p.vt);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int64_t f = n0 + wn * 128 + nb * 32 + li - 2 * d;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int64_t row0 = m0 + wm * 128 + mb * 32 + 8 * b + 4 * hi;  // 4 consecutive rows
+            if (row0 < p.m_pad) {
+              uint32_t w2[2];
+#pragma unroll
+              for (int r2 = 0; r2 < 2; ++r2) {
+                float v0 = acc[mb][nb][4 * b + 2 * r2] * csc[nb];
+                float v1 = acc[mb][nb][4 * b + 2 * r2 + 1] * csc[nb];
+                if (row0 + 2 * r2 >= p.m) v0 = 0.f;
+                if (row0 + 2 * r2 + 1 >= p.m) v1 = 0.f;
+                w2[r2] = static_cast<uint32_t>(f32_to_bf16_bits(v0)) |
+                         (static_cast<uint32_t>(f32_to_bf16_bits(v1)) << 16);
+              }
+              *reinterpret_cast<u32x2*>(vt + f * p.m_pad + row0) = u32x2{w2[0], w2[1]};
+            }
+          }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- float32 kernel
+// Thread (tx, ty) of 16 x 16 owns rows ty + 16i (i < 4) and columns {2tx, 2tx+1, 2tx+32,
+// 2tx+33} of the 64 x 64 tile: RoPE pairs (2tx, 2tx+1) and gate/up partners (c, c+32) are in
+// the same thread.
+template <int kEpi>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
+  constexpr int T = 64, TK = 16;
+  __shared__ float As[TK][T + 1];
+  __shared__ float Bs[TK][T + 1];
+  const float* A = static_cast<const float*>(p.a);
+  const float* W = static_cast<const float*>(p.w);
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * T;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * T;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  int cols[4] = {2 * tx, 2 * tx + 1, 2 * tx + 32, 2 * tx + 33};
+  float acc[4][4] = {};
+  for (int64_t k0 = 0; k0 < p.k; k0 += TK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = threadIdx.x + kThreads * i;  // 0..1023 over [64 rows x 16 k]
+      const int r = e / TK, kk = e % TK;
+      int64_t gr = m0 + r;
+      if (gr >= p.m) gr = p.m - 1;
+      As[kk][r] = A[gr * p.k + k0 + kk];
+      Bs[kk][r] = W[(n0 + r) * p.k + k0 + kk];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][cols[j]];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + ty + 16 * i;
+    if constexpr (kEpi == EPI_F32) {
+      if (row < p.m)
+        for (int j = 0; j < 4; ++j) p.out[row * p.n + n0 + cols[j]] = acc[i][j];
+    } else if constexpr (kEpi == EPI_RESID) {
+      float* x = static_cast<float*>(p.x);
+      if (row < p.m)
+        for (int j = 0; j < 4; ++j) {
+          const int64_t c = n0 + cols[j];
+          x[row * p.n + c] = fmaf(p.gate[c], acc[i][j], x[row * p.n + c]);
+        }
+    } else if constexpr (kEpi == EPI_SWIGLU) {
+      float* h = static_cast<float*>(p.h);
+      const int64_t F = p.n / 2;
+      if (row < p.m)
+        for (int j = 0; j < 2; ++j) {
+          const int64_t f = (n0 / 64) * 32 + cols[j];
+          h[row * F + f] = silu(acc[i][j]) * acc[i][j + 2];
+        }
+    } else {  // EPI_QKV
+      const int64_t d = p.d_model;
+      const int region = static_cast<int>(n0 / d);
+      if (row >= p.m_pad) continue;
+      for (int j = 0; j < 4; ++j) {
+        const int64_t f = n0 + cols[j] - region * d;
+        float out = acc[i][j];
+        if (region < 2 && row < p.geom.n_video) {
+          const int dh = static_cast<int>(f % p.rope.head_dim);
+          const float2 cs = p.rope.table[rope_index(p.rope, row, dh)];
+          out = rope_apply(acc[i][j], acc[i][j ^ 1], cs, (j & 1) == 0);
+        }
+        if (row >= p.m) out = 0.f;
+        if (region == 0) static_cast<float*>(p.q)[row * d + f] = out;
+        else if (region == 1) static_cast<float*>(p.kk)[row * d + f] = out;
+        else static_cast<float*>(p.vt)[f * p.m_pad + row] = out;
+      }
+    }
+  }
+}
+
+template <bool kInt8>
+hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
+  const int tiles_m = static_cast<int>((a.m + BM - 1) / BM);
+  const int tiles_n = static_cast<int>(a.n / BN);
+  const int total = tiles_m * tiles_n;
+  const int grid = (total + 7) / 8 * 8;
+  const int group_m = 8;
+  switch (epi) {
+    case EPI_QKV:
+      gemm_mfma_kernel<kInt8, EPI_QKV><<<grid, kThreads, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      break;
+    case EPI_RESID:
+      gemm_mfma_kernel<kInt8, EPI_RESID><<<grid, kThreads, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      break;
+    case EPI_SWIGLU:
+      gemm_mfma_kernel<kInt8, EPI_SWIGLU><<<grid, kThreads, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      break;
+    default:
+      gemm_mfma_kernel<kInt8, EPI_F32><<<grid, kThreads, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.m == 0) return hipSuccess;
+  if (act == H3X_F32) {
+    dim3 grid(static_cast<unsigned>(a.n / 64), static_cast<unsigned>((a.m + 63) / 64));
+    switch (epi) {
+      case EPI_QKV: gemm_f32_kernel<EPI_QKV><<<grid, kThreads, 0, s>>>(a); break;
+      case EPI_RESID: gemm_f32_kernel<EPI_RESID><<<grid, kThreads, 0, s>>>(a); break;
+      case EPI_SWIGLU: gemm_f32_kernel<EPI_SWIGLU><<<grid, kThreads, 0, s>>>(a); break;
+      default: gemm_f32_kernel<EPI_F32><<<grid, kThreads, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+  }
+  return wdtype == H3X_I8 ? launch_mfma<true>(epi, a, s)
+                          : launch_mfma<false>(epi, a, s);
+}
+
+}  // namespace h3x

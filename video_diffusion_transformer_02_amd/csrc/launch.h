@@ -1,0 +1,68 @@
+// Host-side launchers of the h3x kernels. Each enqueues exactly one kernel on `stream` and
+// returns hipGetLastError() of that launch. Arguments are validated by the caller (api.cpp).
+#pragma once
+
+#include "common.h"
+
+namespace h3x {
+
+// Elementwise and memory-bound kernels (k_elementwise.hip).
+hipError_t launch_norm_mod(int act, int64_t n_rows, int d, float eps, const void* x,
+                           const float* shift, const float* scale, void* y, hipStream_t s);
+hipError_t launch_token_merge(int act, const GeomDev& g, int d, const void* x, void* xm,
+                              hipStream_t s);
+hipError_t launch_token_unmerge(int act, const GeomDev& g, int d, const void* xm, void* x,
+                                hipStream_t s);
+hipError_t launch_euler(int act, int64_t n_elems, float* z, const void* v, float delta,
+                        void* v_copy, hipStream_t s);
+hipError_t launch_assemble(int act, int64_t n_state, int64_t n_text, int d, const float* z,
+                           const void* text, void* x, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_rope_table(const GeomDev& g, int head_dim, float theta, float2* table,
+                             int4* rowbase, hipStream_t s);
+hipError_t launch_pack(int wdtype, int kind, int64_t rows, int64_t cols, const void* w,
+                       void* packed, hipStream_t s);
+hipError_t launch_pack_int8(int kind, int64_t rows, int64_t cols, const void* w_bf16,
+                            int8_t* q, uint16_t* scale, hipStream_t s);
+
+// Source row of packed row p (the gate/up interleave; identity for the other kinds).
+__host__ __device__ inline int64_t packed_source_row(int kind, int64_t p, int64_t rows) {
+  if (kind != H3X_W_GATE_UP) return p;
+  const int64_t f = rows / 2;
+  const int64_t j = p / 64, i = p % 64;
+  return i < 32 ? 32 * j + i : f + 32 * j + (i - 32);
+}
+
+// Contractions. Epilogue kinds of the GEMM kernels.
+enum Epi : int {
+  EPI_QKV = 0,    // RoPE on q, k of video rows; q, k row-major, v transposed; zero pad rows
+  EPI_RESID = 1,  // x += gate * acc
+  EPI_SWIGLU = 2, // h[f] = silu(acc_gate) * acc_up over the 32-row interleave
+  EPI_F32 = 3     // out = acc (float32)
+};
+
+struct GemmArgs {
+  const void* a;        // [m x k] act type, row-major
+  const void* w;        // packed weight [n x k] (bf16, f32 or int8 codes)
+  const uint16_t* wscale;  // int8 scales [n] (bfloat16) or nullptr
+  int64_t m, n, k;
+  int64_t m_pad;        // rows written by EPI_QKV (multiple of 256, >= m)
+  // EPI_QKV
+  void* q; void* kk; void* vt;
+  int32_t d_model;
+  GeomDev geom;
+  RopeDev rope;
+  // EPI_RESID
+  void* x; const float* gate;
+  // EPI_SWIGLU
+  void* h;
+  // EPI_F32
+  float* out;
+};
+
+hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& args, hipStream_t s);
+hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_heads, int head_dim,
+                            const void* q, const void* k, const void* vt, void* o,
+                            hipStream_t s);
+
+}  // namespace h3x
