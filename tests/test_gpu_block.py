@@ -12,6 +12,8 @@ from test_gpu_kernels import SMALL, SMALL_F32, SMALL_I8
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 1e-2, "i8": 2e-2}
+# Larger weights make the residual branches as large as the stream and the attention sharp.
+STRONG = SMALL.replace(name="small_bf16_strong", w_std=0.1, qkv_std=0.1, seed_base=14)
 
 
 @pytest.fixture(scope="module")
@@ -22,7 +24,21 @@ def B():
 
 
 def _tol(wl):
+    if wl.name == STRONG.name:
+        # Logits of std ~5 (weights N(0, 0.1^2)): storing q and k in bfloat16 moves each logit by
+        # about |s| 2^-8, which shifts softmax weights by a few percent. Checked tighter against
+        # the storage-rounded reference below.
+        return 3e-2
     return TOL["i8"] if wl.weight == "i8" else TOL[wl.act]
+
+
+def branch_bound(wl, x, ref):
+    """Tolerance for rel-L2 of (x2 - x): 3x the block tolerance plus two storage roundings of
+    the residual stream (RMS 2^-9/sqrt(3) relative each for bfloat16, 2^-24/sqrt(3) for float32)
+    measured against the branch norm."""
+    unit = 2.0 ** -9 if wl.act == "bf16" else 2.0 ** -24
+    ratio = np.linalg.norm(ref) / max(np.linalg.norm(ref - x), 1e-300)
+    return 3 * _tol(wl) + 2 * unit / np.sqrt(3) * ratio * 1.5
 
 
 def run_block(B, wl, x, b=0, merged=False, mod=None, poison=False):
@@ -38,18 +54,22 @@ def run_block(B, wl, x, b=0, merged=False, mod=None, poison=False):
     return xd, w64, m64
 
 
-@pytest.mark.parametrize("wl", [synth.TINY, synth.TINY_SHARP, SMALL, SMALL_F32, SMALL_I8],
+
+
+@pytest.mark.parametrize("wl", [synth.TINY, synth.TINY_SHARP, SMALL, SMALL_F32, SMALL_I8, STRONG],
                          ids=lambda w: w.name)
 @pytest.mark.parametrize("merged", [False, True])
-def test_block_all_rows(B, wl, merged):
+def test_block_all_rows(B, wl, merged, record):
     og = oracle_geom(wl, merged)
     x = synth.storage_values(synth.normal(wl.seed_base, 77, (og.n_tokens, wl.d_model)), wl.act)
     xd, w64, m64 = run_block(B, wl, x, merged=merged)
     ref = dit.block_forward(x, w64, m64, og, wl.n_heads)
     got = host(xd)
+    record(f"block_all_rows[{wl.name},merged={merged}]", rel_l2(got, ref), _tol(wl))
     assert rel_l2(got, ref) < _tol(wl)
-    # The residual branch alone (x2 - x), which the residual does not dilute.
-    assert rel_l2(got - x, ref - x) < 3 * _tol(wl)
+    # The residual branch alone (x2 - x), which the residual does not dilute: allowed the block
+    # tolerance plus the two roundings of the residual stream (x1, x2) to the storage type.
+    assert rel_l2(got - x, ref - x) < branch_bound(wl, x, ref)
 
 
 def test_block_zero_gates_is_identity_bit_exact(B):
@@ -72,7 +92,7 @@ def test_block_deterministic_and_poisoned_workspace(B):
     assert torch.equal(a, b)
 
 
-def test_block_full_size_sampled_rows(B):
+def test_block_full_size_sampled_rows(B, record):
     """One block at the 6 x 32 x 32 + 256 + 512 token, d = 6144 shape: 64 sampled rows."""
     wl = synth.BLOCK
     og = oracle_geom(wl)
@@ -81,8 +101,9 @@ def test_block_full_size_sampled_rows(B):
     rows = synth.sample_rows(wl)
     ref = dit.block_forward(x, w64, m64, og, wl.n_heads, rows=rows)
     got = host(xd)[rows]
+    record("block_full_size_sampled_rows", rel_l2(got, ref), TOL["bf16"])
     assert rel_l2(got, ref) < TOL["bf16"]
-    assert rel_l2(got - x[rows], ref - x[rows]) < 3 * TOL["bf16"]
+    assert rel_l2(got - x[rows], ref - x[rows]) < branch_bound(wl, x[rows], ref)
 
 
 # ---------------------------------------------------------------- sampler steps
@@ -121,17 +142,19 @@ def _chain(B, wl, n_blocks, n_steps, reuse, tr=(-1, -1), check_every=True):
 
 
 @pytest.mark.parametrize("wl", [synth.TINY, SMALL, SMALL_I8], ids=lambda w: w.name)
-def test_denoise_chain_reuse(B, wl):
+def test_denoise_chain_reuse(B, wl, record):
     n_steps, reuse = (20, 2) if wl.act == "f32" else (4, 2)
     errs = _chain(B, wl, 2, n_steps, reuse)
+    record(f"denoise_chain_reuse[{wl.name}] max dz", max(e[1] for e in errs), 3 * _tol(wl))
     for i, (e_z, e_dz) in enumerate(errs):
         assert e_z < _tol(wl), (i, e_z)
         assert e_dz < 3 * _tol(wl), (i, e_dz)
 
 
 @pytest.mark.parametrize("wl", [SMALL, SMALL_F32], ids=lambda w: w.name)
-def test_denoise_chain_token_reduction(B, wl):
+def test_denoise_chain_token_reduction(B, wl, record):
     errs = _chain(B, wl, 4, 3, 1, tr=(1, 2))
+    record(f"denoise_chain_tr[{wl.name}] max dz", max(e[1] for e in errs), 3 * _tol(wl))
     for i, (e_z, e_dz) in enumerate(errs):
         assert e_z < _tol(wl), (i, e_z)
         assert e_dz < 3 * _tol(wl), (i, e_dz)
@@ -149,3 +172,33 @@ def test_denoise_reused_step_reads_cache_only(B):
     torch.cuda.synchronize()
     ref = sampler.euler_update(z, sampler.sigma_delta(0.95, 0.9), v)
     np.testing.assert_array_equal(zd.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def storage_rounded_block(x, w, mod, geom, n_heads):
+    """The block with every stored activation (y, q, k, v, o, x1, y2, h, x2) rounded to bfloat16,
+    built from the oracle's primitives: a tighter reference for the bf16 kernels' arithmetic."""
+    from oracle.numeric import round_storage as r
+    d = x.shape[1]
+    shift1, scale1, gate1, shift2, scale2, gate2 = mod
+    pos, rot = geom.positions()
+    f64 = lambda a: np.asarray(a, np.float64)
+    y = f64(r(dit.rms_norm_mod(x, shift1, scale1), "bf16"))
+    q = f64(r(dit.rope(y @ w["qkv"][:d].T, pos, rot, n_heads), "bf16"))
+    k = f64(r(dit.rope(y @ w["qkv"][d:2 * d].T, pos, rot, n_heads), "bf16"))
+    v = f64(r(y @ w["qkv"][2 * d:].T, "bf16"))
+    o = f64(r(dit.attention(q, k, v, n_heads), "bf16"))
+    x1 = f64(r(x + gate1 * (o @ w["out"].T), "bf16"))
+    y2 = f64(r(dit.rms_norm_mod(x1, shift2, scale2), "bf16"))
+    h = f64(r(dit.silu(y2 @ w["gate"].T) * (y2 @ w["up"].T), "bf16"))
+    return f64(r(x1 + gate2 * (h @ w["down"].T), "bf16"))
+
+
+def test_block_strong_vs_storage_rounded(B, record):
+    wl = STRONG
+    og = oracle_geom(wl)
+    x = synth.storage_values(synth.normal(wl.seed_base, 77, (og.n_tokens, wl.d_model)), "bf16")
+    xd, w64, m64 = run_block(B, wl, x)
+    ref = storage_rounded_block(x, w64, m64, og, wl.n_heads)
+    e = rel_l2(host(xd), ref)
+    record("block_strong_vs_storage_rounded", e, 1e-2)
+    assert e < 1e-2

@@ -103,50 +103,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
   const int64_t K = p.k;
   const int ktiles = static_cast<int>(K / BK);
 
-  const uint16_t* A = static_cast<const uint16_t*>(p.a);
-  const uint8_t* Wb = static_cast<const uint8_t*>(p.w);
+  // ---- global -> LDS without registers: buffer_load_dwordx4 ... lds writes lane l's 16 bytes
+  // at (wave-uniform base) + 16 l. Each wave instruction fills 1 KB of a stage: 8 A rows (or
+  // bf16 B rows, 128 bytes each) or 16 int8 B rows (64 bytes each); the lane picks the global
+  // chunk that the XOR swizzle places at its LDS position. Rows past the end of A lie outside
+  // the buffer's range and read as zeros.
+  const uint8_t* Ab = static_cast<const uint8_t*>(p.a) + m0 * K * 2;
+  const uint8_t* Wb = static_cast<const uint8_t*>(p.w) + n0 * K * (kInt8 ? 1 : 2);
+  const int64_t a_rows = p.m - m0 < BM ? p.m - m0 : BM;
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Ab), 0, static_cast<int>(a_rows * K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Wb), 0, static_cast<int>(BN * K * (kInt8 ? 1 : 2)), 0x00020000);
+  // Row and chunk of this lane within its 1 KB piece.
+  const int a_row = lane >> 3, a_chunk = (lane & 7) ^ (lane >> 3);
+  const uint32_t a_voff = static_cast<uint32_t>((wave * 8 + a_row) * K * 2 + a_chunk * 16);
+  const int b8_row = lane >> 2, b8_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t b_voff = kInt8 ? static_cast<uint32_t>((wave * 16 + b8_row) * K + b8_chunk * 16) : a_voff;
+  const uint32_t a_step = static_cast<uint32_t>(32 * K * 2);                 // 32 rows
+  const uint32_t b_step = kInt8 ? static_cast<uint32_t>(64 * K) : a_step;   // 64 int8 rows
 
-  // ---- global -> register staging
-  u32x4 ra[8];
-  u32x4 rb[kInt8 ? 4 : 8];
-  auto load_tiles = [&](int kt) {
-    const int64_t k0 = static_cast<int64_t>(kt) * BK;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      int64_t gr = m0 + row;
-      if (gr >= p.m) gr = p.m - 1;  // clamp: rows past the end are computed but never stored
-      ra[i] = *reinterpret_cast<const u32x4*>(A + gr * K + k0 + (tid & 7) * 8);
-    }
-    if constexpr (kInt8) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 2) + 64 * i;
-        rb[i] = *reinterpret_cast<const u32x4*>(Wb + (n0 + row) * K + k0 + (tid & 3) * 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = (tid >> 3) + 32 * i;
-        rb[i] = *reinterpret_cast<const u32x4*>(Wb + ((n0 + row) * K + k0 + (tid & 7) * 8) * 2);
-      }
-    }
-  };
-  auto store_tiles = [&](int stage) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto issue_loads = [&](int kt, int stage) {
     uint8_t* sa = smem + stage * (Smem<kInt8>::kA + Smem<kInt8>::kB);
     uint8_t* sb = sa + Smem<kInt8>::kA;
+    const uint32_t ka = static_cast<uint32_t>(kt) * BK * 2;
+    const uint32_t kb = static_cast<uint32_t>(kt) * BK * (kInt8 ? 1 : 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(sa + swz16((tid >> 3) + 32 * i, tid & 7)) = ra[i];
-    if constexpr (kInt8) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(sa + (4 * i + wave) * 1024), 16,
+                                               a_voff + i * a_step, ka, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(sb + swz8((tid >> 2) + 64 * i, tid & 3)) = rb[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(sb + swz16((tid >> 3) + 32 * i, tid & 7)) = rb[i];
-    }
+    for (int i = 0; i < (kInt8 ? 4 : 8); ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_ptr)(sb + (4 * i + wave) * 1024), 16,
+                                               b_voff + i * b_step, kb, 0, 0);
   };
 
   f32x16 acc[4][4];
@@ -157,41 +147,88 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < ktiles) load_tiles(kt + 1);
+  // Operand fragments of one 16-wide K slice: A rows of the four m-blocks, B rows of the four
+  // n-blocks (int8 weights stay packed until just before the multiply).
+  struct Frags {
+    bf16x8 a[4];
+    u32x4 b[4];  // bf16: 8 values; int8: 8 codes in .xy
+  };
+  auto read_frags = [&](int stage, int ks, Frags& f) {
     const uint8_t* sa = smem + stage * (Smem<kInt8>::kA + Smem<kInt8>::kB);
     const uint8_t* sb = sa + Smem<kInt8>::kA;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bfr[4];
+    for (int mb = 0; mb < 4; ++mb)
+      f.a[mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + swz16(wm * 128 + mb * 32 + li, 2 * ks + hi)));
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int row = wm * 128 + mb * 32 + li;
-        af[mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + swz16(row, 2 * ks + hi)));
+    for (int nb = 0; nb < 4; ++nb) {
+      const int row = wn * 128 + nb * 32 + li;
+      if constexpr (kInt8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(sb + swz8(row, ks) + 8 * hi);
+        f.b[nb] = u32x4{v.x, v.y, 0u, 0u};
+      } else {
+        f.b[nb] = *reinterpret_cast<const u32x4*>(sb + swz16(row, 2 * ks + hi));
       }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int row = wn * 128 + nb * 32 + li;
-        if constexpr (kInt8) {
-          bfr[nb] = widen_i8(*reinterpret_cast<const u32x2*>(sb + swz8(row, ks) + 8 * hi));
-        } else {
-          bfr[nb] = as_bf16x8(*reinterpret_cast<const u32x4*>(sb + swz16(row, 2 * ks + hi)));
-        }
-      }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
     }
-    if (kt + 1 < ktiles) store_tiles(stage ^ 1);
+  };
+  auto mma = [&](const Frags& f) {
+    bf16x8 bv[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      if constexpr (kInt8) bv[nb] = widen_i8(u32x2{f.b[nb].x, f.b[nb].y});
+      else bv[nb] = as_bf16x8(f.b[nb]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+  };
+
+  // Software pipeline, one barrier per K step. While the four 16-wide slices of K step kt are
+  // multiplied, the fragments of the next slice are read from LDS and K step kt+1 streams into
+  // the other LDS stage. The scheduling groups interleave one LDS read (and the stream's
+  // buffer loads) between consecutive MFMAs so that the matrix pipe is never left waiting.
+  constexpr int kLoads = kInt8 ? 12 : 16;
+  Frags f0, f1;
+  auto interleave = [&]<int kVmem>() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if constexpr (kVmem > 0) __builtin_amdgcn_sched_group_barrier(0x020, kVmem, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);  // nothing crosses: keeps each slice's MFMAs together
+  };
+  auto k_step = [&]<bool kNext>(int kt) {
+    const int stage = kt & 1;
+    read_frags(stage, 1, f1);
+    if constexpr (kNext) issue_loads(kt + 1, stage ^ 1);
+    mma(f0);
+    interleave.template operator()<kNext ? (kLoads + 7) / 8 : 0>();
+    read_frags(stage, 2, f0);
+    mma(f1);
+    interleave.template operator()<0>();
+    read_frags(stage, 3, f1);
+    mma(f0);
+    interleave.template operator()<0>();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-  }
+    if constexpr (kNext) {
+      read_frags(stage ^ 1, 0, f0);
+      mma(f1);
+      interleave.template operator()<0>();
+    } else {
+      mma(f1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue_loads(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  read_frags(0, 0, f0);
+  for (int kt = 0; kt + 1 < ktiles; ++kt) k_step.template operator()<true>(kt);
+  k_step.template operator()<false>(ktiles - 1);
 
   // ---- epilogue. Element (mb, nb, 4b + r) of this lane: row m0 + wm*128 + mb*32 + 8b + 4hi + r,
   // column n0 + wn*128 + nb*32 + li.
@@ -417,7 +454,9 @@ hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.m == 0) return hipSuccess;
   if (act == H3X_F32) {
-    dim3 grid(static_cast<unsigned>(a.n / 64), static_cast<unsigned>((a.m + 63) / 64));
+    // EPI_QKV also writes the zero pad rows m .. m_pad-1 of q, k and v^T.
+    const int64_t rows = epi == EPI_QKV ? a.m_pad : a.m;
+    dim3 grid(static_cast<unsigned>(a.n / 64), static_cast<unsigned>((rows + 63) / 64));
     switch (epi) {
       case EPI_QKV: gemm_f32_kernel<EPI_QKV><<<grid, kThreads, 0, s>>>(a); break;
       case EPI_RESID: gemm_f32_kernel<EPI_RESID><<<grid, kThreads, 0, s>>>(a); break;
