@@ -230,113 +230,183 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
   for (int kt = 0; kt + 1 < ktiles; ++kt) k_step.template operator()<true>(kt);
   k_step.template operator()<false>(ktiles - 1);
 
-  // ---- epilogue. Element (mb, nb, 4b + r) of this lane: row m0 + wm*128 + mb*32 + 8b + 4hi + r,
-  // column n0 + wn*128 + nb*32 + li.
-  float csc[4];
+  // ---- epilogue through LDS. Each wave stages its 128 x 128 float32 result 32 rows at a time
+  // (row stride 136 floats: the two half-waves of an MFMA block store to disjoint banks), then
+  // reads it back row-wise (8 consecutive columns per lane: RoPE pairs and 16-byte stores) or,
+  // for the transposed v, column-wise. Element (mb, nb, 4b + r) of a lane sits at row
+  // 8b + 4hi + r of slice mb and column nb*32 + li of the wave's sub-tile.
+  constexpr int kStride = 136;
+  float* st = reinterpret_cast<float*>(smem) + wave * 32 * kStride;
+  const int64_t row_base = m0 + wm * 128;
+  const int64_t col_base = n0 + wn * 128;
+  const int lc = (lane & 15) * 8;  // first of this lane's 8 columns in row-wise passes
+  float csc[8];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int64_t col = n0 + wn * 128 + nb * 32 + li;
-    csc[nb] = kInt8 ? bf16_bits_to_f32(p.wscale[col]) : 1.0f;
+  for (int j = 0; j < 8; ++j) csc[j] = 1.0f;
+  if constexpr (kInt8) {
+    if constexpr (kEpi == EPI_SWIGLU) {
+      // gate and up scales of this lane's columns (see the SwiGLU pass below)
+    } else {
+      const u32x4 sraw = *reinterpret_cast<const u32x4*>(p.wscale + col_base + lc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        csc[2 * j] = __uint_as_float(sraw[j] << 16);
+        csc[2 * j + 1] = __uint_as_float(sraw[j] & 0xffff0000u);
+      }
+    }
   }
 
-  if constexpr (kEpi == EPI_F32) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-          const int64_t col = n0 + wn * 128 + nb * 32 + li;
-          if (row < p.m) p.out[row * p.n + col] = acc[mb][nb][e] * csc[nb];
-        }
-  } else if constexpr (kEpi == EPI_RESID) {
-    uint16_t* x = static_cast<uint16_t*>(p.x);
-    float g[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) g[nb] = p.gate[n0 + wn * 128 + nb * 32 + li] * csc[nb];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+      for (int e = 0; e < 16; ++e)
+        st[(8 * (e >> 2) + 4 * hi + (e & 3)) * kStride + nb * 32 + li] = acc[mb][nb][e];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int64_t r0 = row_base + mb * 32;
+
+    if constexpr (kEpi == EPI_F32 || kEpi == EPI_RESID) {
+#pragma unroll 2
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 4 + (lane >> 4);
+        const int64_t row = r0 + r;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc + 4);
+        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         if (row < p.m) {
+          if constexpr (kEpi == EPI_F32) {
+            float* o = p.out + row * p.n + col_base + lc;
+            *reinterpret_cast<f32x4*>(o) = f32x4{v[0] * csc[0], v[1] * csc[1], v[2] * csc[2], v[3] * csc[3]};
+            *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4] * csc[4], v[5] * csc[5], v[6] * csc[6], v[7] * csc[7]};
+          } else {
+            uint16_t* xp = static_cast<uint16_t*>(p.x) + row * p.n + col_base + lc;
+            const u32x4 xr = *reinterpret_cast<const u32x4*>(xp);
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(p.gate + col_base + lc);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(p.gate + col_base + lc + 4);
+            const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+            u32x4 out;
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            const int64_t idx = row * p.n + n0 + wn * 128 + nb * 32 + li;
-            x[idx] = f32_to_bf16_bits(fmaf(g[nb], acc[mb][nb][e], bf16_bits_to_f32(x[idx])));
+            for (int j = 0; j < 4; ++j) {
+              const float x0 = __uint_as_float(xr[j] << 16), x1 = __uint_as_float(xr[j] & 0xffff0000u);
+              const float y0 = fmaf(g[2 * j] * csc[2 * j], v[2 * j], x0);
+              const float y1 = fmaf(g[2 * j + 1] * csc[2 * j + 1], v[2 * j + 1], x1);
+              out[j] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
+                       (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+            }
+            *reinterpret_cast<u32x4*>(xp) = out;
           }
         }
       }
-  } else if constexpr (kEpi == EPI_SWIGLU) {
-    uint16_t* h = static_cast<uint16_t*>(p.h);
-    const int64_t F = p.n / 2;
+    } else if constexpr (kEpi == EPI_SWIGLU) {
+      // 128 packed columns = two groups of [32 gate | 32 up] -> 64 h features per row.
+      const int hc = (lane & 7) * 8;              // this lane's first h feature within the 64
+      const int grp = hc / 32, ih = hc % 32;
+      const int gcol = grp * 64 + ih, ucol = gcol + 32;
+      float sg[8], su[8];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int j = 0; j < 8; ++j) { sg[j] = 1.0f; su[j] = 1.0f; }
+      if constexpr (kInt8) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(p.wscale + col_base + gcol);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(p.wscale + col_base + ucol);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        for (int j = 0; j < 4; ++j) {
+          sg[2 * j] = __uint_as_float(a[j] << 16); sg[2 * j + 1] = __uint_as_float(a[j] & 0xffff0000u);
+          su[2 * j] = __uint_as_float(b[j] << 16); su[2 * j + 1] = __uint_as_float(b[j] & 0xffff0000u);
+        }
+      }
+      const int64_t F = p.n / 2;
+      const int64_t f0 = col_base / 2 + hc;
+#pragma unroll 2
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int64_t row = r0 + r;
+        const f32x4 ga = *reinterpret_cast<const f32x4*>(st + r * kStride + gcol);
+        const f32x4 gb = *reinterpret_cast<const f32x4*>(st + r * kStride + gcol + 4);
+        const f32x4 ua = *reinterpret_cast<const f32x4*>(st + r * kStride + ucol);
+        const f32x4 ub = *reinterpret_cast<const f32x4*>(st + r * kStride + ucol + 4);
+        const float gv[8] = {ga[0], ga[1], ga[2], ga[3], gb[0], gb[1], gb[2], gb[3]};
+        const float uv[8] = {ua[0], ua[1], ua[2], ua[3], ub[0], ub[1], ub[2], ub[3]};
         if (row < p.m) {
+          u32x4 out;
 #pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const int64_t col = n0 + wn * 128 + pr * 64;  // multiple of 64: gate block, then up
-            const int64_t f = (col / 64) * 32 + li;
-            const float gv = acc[mb][2 * pr][e] * csc[2 * pr];
-            const float uv = acc[mb][2 * pr + 1][e] * csc[2 * pr + 1];
-            h[row * F + f] = f32_to_bf16_bits(silu(gv) * uv);
+          for (int j = 0; j < 4; ++j) {
+            const float h0 = silu(gv[2 * j] * sg[2 * j]) * (uv[2 * j] * su[2 * j]);
+            const float h1 = silu(gv[2 * j + 1] * sg[2 * j + 1]) * (uv[2 * j + 1] * su[2 * j + 1]);
+            out[j] = static_cast<uint32_t>(f32_to_bf16_bits(h0)) |
+                     (static_cast<uint32_t>(f32_to_bf16_bits(h1)) << 16);
           }
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.h) + row * F + f0) = out;
         }
       }
-  } else {  // EPI_QKV
-    const int64_t d = p.d_model;
-    const int region = static_cast<int>(n0 / d);  // 0 = q, 1 = k, 2 = v (d % 256 == 0)
-    if (region < 2) {
-      uint16_t* dst = static_cast<uint16_t*>(region == 0 ? p.q : p.kk);
-      const bool even = (li & 1) == 0;
+    } else {  // EPI_QKV
+      const int64_t d = p.d_model;
+      const int region = static_cast<int>(n0 / d);  // 0 = q, 1 = k, 2 = v (d % 256 == 0)
+      if (region < 2) {
+        uint16_t* dst = static_cast<uint16_t*>(region == 0 ? p.q : p.kk);
+        const int64_t f = col_base + lc - region * d;        // first of 8 features
+        const int dh = static_cast<int>(f % p.rope.head_dim);  // the 8 lie in one RoPE chunk
+        const int ct = p.rope.head_dim / 4, cy = 3 * p.rope.head_dim / 8;
+        const int axis = dh < ct ? 0 : (dh < ct + cy ? 1 : 2);
+        const int k0 = axis == 0 ? dh / 2 : (axis == 1 ? (dh - ct) / 2 : (dh - ct - cy) / 2);
+#pragma unroll 2
+        for (int it = 0; it < 8; ++it) {
+          const int r = it * 4 + (lane >> 4);
+          const int64_t row = r0 + r;
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc + 4);
+          float v[8] = {v0[0] * csc[0], v0[1] * csc[1], v0[2] * csc[2], v0[3] * csc[3],
+                        v1[0] * csc[4], v1[1] * csc[5], v1[2] * csc[6], v1[3] * csc[7]};
+          if (row < p.geom.n_video) {
+            const int4 rb = p.rope.rowbase[row];
+            const int base = (axis == 0 ? rb.x : (axis == 1 ? rb.y : rb.z)) + k0;
+            const f32x4 cs01 = *reinterpret_cast<const f32x4*>(p.rope.table + base);
+            const f32x4 cs23 = *reinterpret_cast<const f32x4*>(p.rope.table + base + 2);
+            const float c[4] = {cs01[0], cs01[2], cs23[0], cs23[2]};
+            const float sn[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int64_t f = n0 + wn * 128 + nb * 32 + li - region * d;
-        const int dh = static_cast<int>(f % p.rope.head_dim);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-            const float v = acc[mb][nb][e] * csc[nb];
-            const float partner = dpp_swap_adjacent(v);
-            float out = v;
-            if (row < p.geom.n_video) {
-              const float2 cs = p.rope.table[rope_index(p.rope, row, dh)];
-              out = rope_apply(v, partner, cs, even);
-            }
-            if (row >= p.m) out = 0.f;
-            if (row < p.m_pad) dst[row * d + f] = f32_to_bf16_bits(out);
-          }
-      }
-    } else {
-      uint16_t* vt = static_cast<uint16_t*>(p.vt);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int64_t f = n0 + wn * 128 + nb * 32 + li - 2 * d;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int64_t row0 = m0 + wm * 128 + mb * 32 + 8 * b + 4 * hi;  // 4 consecutive rows
-            if (row0 < p.m_pad) {
-              uint32_t w2[2];
-#pragma unroll
-              for (int r2 = 0; r2 < 2; ++r2) {
-                float v0 = acc[mb][nb][4 * b + 2 * r2] * csc[nb];
-                float v1 = acc[mb][nb][4 * b + 2 * r2 + 1] * csc[nb];
-                if (row0 + 2 * r2 >= p.m) v0 = 0.f;
-                if (row0 + 2 * r2 + 1 >= p.m) v1 = 0.f;
-                w2[r2] = static_cast<uint32_t>(f32_to_bf16_bits(v0)) |
-                         (static_cast<uint32_t>(f32_to_bf16_bits(v1)) << 16);
-              }
-              *reinterpret_cast<u32x2*>(vt + f * p.m_pad + row0) = u32x2{w2[0], w2[1]};
+            for (int j = 0; j < 4; ++j) {
+              const float a = v[2 * j], b = v[2 * j + 1];
+              v[2 * j] = fmaf(a, c[j], -b * sn[j]);
+              v[2 * j + 1] = fmaf(a, sn[j], b * c[j]);
             }
           }
+          if (row < p.m_pad) {
+            u32x4 out;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float y0 = row < p.m ? v[2 * j] : 0.f, y1 = row < p.m ? v[2 * j + 1] : 0.f;
+              out[j] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
+                       (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+            }
+            *reinterpret_cast<u32x4*>(dst + row * d + f) = out;
+          }
+        }
+      } else {
+        // v transposed: each lane walks one column (feature) down the 32 staged rows and writes
+        // them as 64 contiguous bytes of v^T.
+        uint16_t* vt = static_cast<uint16_t*>(p.vt);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int c = lane + 64 * half;
+          const int64_t f = col_base + c - 2 * d;
+          float sc = 1.0f;
+          if constexpr (kInt8) sc = bf16_bits_to_f32(p.wscale[col_base + c]);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            u32x4 out;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = q4 * 8 + 2 * j;
+              const float y0 = r0 + r < p.m ? st[r * kStride + c] * sc : 0.f;
+              const float y1 = r0 + r + 1 < p.m ? st[(r + 1) * kStride + c] * sc : 0.f;
+              out[j] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
+                       (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
+            }
+            *reinterpret_cast<u32x4*>(vt + f * p.m_pad + r0 + q4 * 8) = out;
+          }
+        }
       }
     }
   }
