@@ -22,7 +22,7 @@ namespace h3x {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32, kStages = 4;
 
 // ---------------------------------------------------------------- shared epilogue math
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -49,17 +49,19 @@ __device__ __forceinline__ float dpp_swap_adjacent(float v) {
 // ---------------------------------------------------------------- MFMA kernel
 template <bool kInt8>
 struct Smem {
-  static constexpr int kA = BM * BK * 2;                 // bytes of one A stage
-  static constexpr int kB = BN * BK * (kInt8 ? 1 : 2);   // bytes of one B stage
-  static constexpr int kTotal = 2 * (kA + kB);
+  static constexpr int kA = BM * BK * 2;                 // bytes of one A stage (16 KB)
+  static constexpr int kB = BN * BK * (kInt8 ? 1 : 2);   // bytes of one B stage (16 / 8 KB)
+  static constexpr int kStage = kA + kB;
+  static constexpr int kTotal = kStages * kStage;
 };
 
-// LDS byte offset of 16-byte chunk c (0..7) of bf16 row `row` in a [rows x 64] tile.
-__device__ __forceinline__ int swz16(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
-// LDS byte offset of 16-byte chunk c (0..3) of int8 row `row` in a [rows x 64] tile.
-__device__ __forceinline__ int swz8(int row, int c) {
-  return row * 64 + ((c ^ ((row >> 2) & 3)) << 4);
-}
+// LDS byte offset of 16-byte chunk c (0..3) of a 64-byte bf16 row (32 values). Rows r and r+4
+// share banks, so the chunk index is flipped by bits 2..3 of the row: any 8 consecutive rows
+// read at one chunk hit 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz16(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..1) of a 32-byte int8 row (32 codes); rows r and r+8
+// share banks, so bit 3 of the row flips the chunk.
+__device__ __forceinline__ int swz8(int row, int c) { return row * 32 + ((c ^ ((row >> 3) & 1)) << 4); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -75,6 +77,22 @@ __device__ __forceinline__ bf16x8 widen_i8(u32x2 v) {
     o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
   }
   return as_bf16x8(u32x4{o[0], o[1], o[2], o[3]});
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the LDS pipeline: this wave's LDS reads are complete (so no stage it
+// read can be overwritten under it) and at most N of its global->LDS loads are in flight; the
+// loads that remain in flight target stages nobody reads before a later barrier. (A plain
+// __syncthreads would also drain every outstanding global->LDS load.)
+template <int N>
+__device__ __forceinline__ void pipeline_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <bool kInt8, int kEpi>
@@ -104,10 +122,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
   const int ktiles = static_cast<int>(K / BK);
 
   // ---- global -> LDS without registers: buffer_load_dwordx4 ... lds writes lane l's 16 bytes
-  // at (wave-uniform base) + 16 l. Each wave instruction fills 1 KB of a stage: 8 A rows (or
-  // bf16 B rows, 128 bytes each) or 16 int8 B rows (64 bytes each); the lane picks the global
-  // chunk that the XOR swizzle places at its LDS position. Rows past the end of A lie outside
-  // the buffer's range and read as zeros.
+  // at (wave-uniform base) + 16 l. One wave instruction fills 1 KB of a stage: 16 bf16 rows of
+  // 64 bytes, or 32 int8 rows of 32 bytes; each lane fetches the global chunk that the swizzle
+  // places at its LDS position. Rows past the end of A lie outside the buffer's range and read
+  // as zeros.
   const uint8_t* Ab = static_cast<const uint8_t*>(p.a) + m0 * K * 2;
   const uint8_t* Wb = static_cast<const uint8_t*>(p.w) + n0 * K * (kInt8 ? 1 : 2);
   const int64_t a_rows = p.m - m0 < BM ? p.m - m0 : BM;
@@ -115,26 +133,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
       const_cast<uint8_t*>(Ab), 0, static_cast<int>(a_rows * K * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(Wb), 0, static_cast<int>(BN * K * (kInt8 ? 1 : 2)), 0x00020000);
-  // Row and chunk of this lane within its 1 KB piece.
-  const int a_row = lane >> 3, a_chunk = (lane & 7) ^ (lane >> 3);
-  const uint32_t a_voff = static_cast<uint32_t>((wave * 8 + a_row) * K * 2 + a_chunk * 16);
-  const int b8_row = lane >> 2, b8_chunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const uint32_t b_voff = kInt8 ? static_cast<uint32_t>((wave * 16 + b8_row) * K + b8_chunk * 16) : a_voff;
-  const uint32_t a_step = static_cast<uint32_t>(32 * K * 2);                 // 32 rows
-  const uint32_t b_step = kInt8 ? static_cast<uint32_t>(64 * K) : a_step;   // 64 int8 rows
+  const int a_row = lane >> 2, a_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t a_voff = static_cast<uint32_t>((wave * 16 + a_row) * K * 2 + a_chunk * 16);
+  const int b8_row = lane >> 1, b8_chunk = (lane & 1) ^ ((lane >> 4) & 1);
+  const uint32_t b_voff = kInt8 ? static_cast<uint32_t>((wave * 32 + b8_row) * K + b8_chunk * 16) : a_voff;
+  const uint32_t a_step = static_cast<uint32_t>(64 * K * 2);                // 64 rows
+  const uint32_t b_step = kInt8 ? static_cast<uint32_t>(128 * K) : a_step;  // 128 int8 rows
+  constexpr int kLoadsA = Smem<kInt8>::kA / 1024 / 4;  // per thread per stage
+  constexpr int kLoadsB = Smem<kInt8>::kB / 1024 / 4;
+  constexpr int kLoads = kLoadsA + kLoadsB;
 
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  auto issue_loads = [&](int kt, int stage) {
-    uint8_t* sa = smem + stage * (Smem<kInt8>::kA + Smem<kInt8>::kB);
+  auto issue_loads = [&](int kt) {
+    uint8_t* sa = smem + (kt % kStages) * Smem<kInt8>::kStage;
     uint8_t* sb = sa + Smem<kInt8>::kA;
     const uint32_t ka = static_cast<uint32_t>(kt) * BK * 2;
     const uint32_t kb = static_cast<uint32_t>(kt) * BK * (kInt8 ? 1 : 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kLoadsA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(sa + (4 * i + wave) * 1024), 16,
                                                a_voff + i * a_step, ka, 0, 0);
 #pragma unroll
-    for (int i = 0; i < (kInt8 ? 4 : 8); ++i)
+    for (int i = 0; i < kLoadsB; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_ptr)(sb + (4 * i + wave) * 1024), 16,
                                                b_voff + i * b_step, kb, 0, 0);
   };
@@ -153,20 +173,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
     bf16x8 a[4];
     u32x4 b[4];  // bf16: 8 values; int8: 8 codes in .xy
   };
-  auto read_frags = [&](int stage, int ks, Frags& f) {
-    const uint8_t* sa = smem + stage * (Smem<kInt8>::kA + Smem<kInt8>::kB);
+  auto read_frags = [&](int kt, int slice, Frags& f) {
+    const uint8_t* sa = smem + (kt % kStages) * Smem<kInt8>::kStage;
     const uint8_t* sb = sa + Smem<kInt8>::kA;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      f.a[mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + swz16(wm * 128 + mb * 32 + li, 2 * ks + hi)));
+      f.a[mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + swz16(wm * 128 + mb * 32 + li, 2 * slice + hi)));
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int row = wn * 128 + nb * 32 + li;
       if constexpr (kInt8) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(sb + swz8(row, ks) + 8 * hi);
+        const u32x2 v = *reinterpret_cast<const u32x2*>(sb + swz8(row, slice) + 8 * hi);
         f.b[nb] = u32x4{v.x, v.y, 0u, 0u};
       } else {
-        f.b[nb] = *reinterpret_cast<const u32x4*>(sb + swz16(row, 2 * ks + hi));
+        f.b[nb] = *reinterpret_cast<const u32x4*>(sb + swz16(row, 2 * slice + hi));
       }
     }
   };
@@ -183,13 +203,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
       for (int nb = 0; nb < 4; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bv[nb], acc[mb][nb], 0, 0, 0);
   };
-
-  // Software pipeline, one barrier per K step. While the four 16-wide slices of K step kt are
-  // multiplied, the fragments of the next slice are read from LDS and K step kt+1 streams into
-  // the other LDS stage. The scheduling groups interleave one LDS read (and the stream's
-  // buffer loads) between consecutive MFMAs so that the matrix pipe is never left waiting.
-  constexpr int kLoads = kInt8 ? 12 : 16;
-  Frags f0, f1;
+  // One LDS read between consecutive MFMAs for the first half of a slice, the rest of the
+  // MFMAs back to back; kVmem buffer loads ride along with each of the first eight MFMAs.
   auto interleave = [&]<int kVmem>() {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -200,35 +215,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);  // nothing crosses: keeps each slice's MFMAs together
   };
-  auto k_step = [&]<bool kNext>(int kt) {
-    const int stage = kt & 1;
-    read_frags(stage, 1, f1);
-    if constexpr (kNext) issue_loads(kt + 1, stage ^ 1);
+
+  // Four LDS stages, K step 32 (two 16-wide slices), one barrier per K step. K step kt+3
+  // streams into the stage that K step kt-1 left while kt is multiplied; the fragments of the
+  // next slice are read while the current one is multiplied. kAhead = K steps issued beyond
+  // kt+1 (2 in steady state), so waiting for vmcnt <= kAhead * kLoads leaves step kt+1 landed.
+  Frags f0, f1;
+  auto k_step = [&]<int kAhead>(int kt) {
+    read_frags(kt, 1, f1);
+    if constexpr (kAhead == 2) issue_loads(kt + 3);
     mma(f0);
-    interleave.template operator()<kNext ? (kLoads + 7) / 8 : 0>();
-    read_frags(stage, 2, f0);
+    interleave.template operator()<kAhead == 2 ? (kLoads + 7) / 8 : 0>();
+    pipeline_barrier<(kAhead > 0 ? kAhead : 0) * kLoads>();
+    if constexpr (kAhead >= 0) read_frags(kt + 1, 0, f0);
     mma(f1);
     interleave.template operator()<0>();
-    read_frags(stage, 3, f1);
-    mma(f0);
-    interleave.template operator()<0>();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if constexpr (kNext) {
-      read_frags(stage ^ 1, 0, f0);
-      mma(f1);
-      interleave.template operator()<0>();
-    } else {
-      mma(f1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   };
-  issue_loads(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  const int pre = ktiles < kStages - 1 ? ktiles : kStages - 1;
+  for (int t = 0; t < pre; ++t) issue_loads(t);
+  if (pre == 3) pipeline_barrier<2 * kLoads>();
+  else if (pre == 2) pipeline_barrier<kLoads>();
+  else pipeline_barrier<0>();
   read_frags(0, 0, f0);
-  for (int kt = 0; kt + 1 < ktiles; ++kt) k_step.template operator()<true>(kt);
-  k_step.template operator()<false>(ktiles - 1);
+  int kt = 0;
+  for (; kt + 3 < ktiles; ++kt) k_step.template operator()<2>(kt);
+  if (kt + 2 < ktiles) k_step.template operator()<1>(kt++);
+  if (kt + 1 < ktiles) k_step.template operator()<0>(kt++);
+  k_step.template operator()<-1>(kt);
 
   // ---- epilogue through LDS. Each wave stages its 128 x 128 float32 result 32 rows at a time
   // (row stride 136 floats: the two half-waves of an MFMA block store to disjoint banks), then
