@@ -15,6 +15,7 @@
 // Epilogues: QKV (3D RoPE on video rows of q and k, v written transposed, pad rows zeroed),
 // gated residual (x += gate * acc), SwiGLU over the 32-row gate/up interleave, float32 store.
 #include <math.h>
+#include <stdlib.h>
 
 #include "launch.h"
 
@@ -22,7 +23,11 @@ namespace h3x {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 256, BK = 32, kStages = 4;
+constexpr int BM = 256, BN = 256, BK = 32;
+#ifndef H3X_GEMM_STAGES
+#define H3X_GEMM_STAGES 5
+#endif
+constexpr int kStages = H3X_GEMM_STAGES;  // LDS stages of the K pipeline (32 KB each for bf16)
 
 // ---------------------------------------------------------------- shared epilogue math
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -95,9 +100,22 @@ __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <bool kInt8, int kEpi>
-__global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int tiles_m,
-                                                                  int tiles_n, int group_m) {
+// Waves of a workgroup: 2 along M, kWN along N. kWN = 2: four waves, each a 128 x 128 sub-tile
+// (256 accumulator registers, one wave per SIMD). kWN = 4: eight waves, each 128 x 64 (128
+// accumulator registers, two waves per SIMD, so one wave's MFMAs can run while the other waits).
+template <int kWN>
+struct Layout {
+  static constexpr int kWaves = 2 * kWN;
+  static constexpr int kThreadsT = 64 * kWaves;
+  static constexpr int SN = BN / kWN;  // columns per wave
+  static constexpr int NB = SN / 32;   // 32-wide MFMA blocks per wave along N
+};
+
+template <bool kInt8, int kEpi, int kWN>
+__global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(GemmArgs p, int tiles_m,
+                                                                                int tiles_n, int group_m) {
+  using L = Layout<kWN>;
+  constexpr int NB = L::NB, SN = L::SN, kWaves = L::kWaves;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<kInt8>::kTotal];
 
   // ---- tile selection: XCD-contiguous runs of a grouped (m-group, n) order
@@ -116,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int li = lane & 31, hi = lane >> 5;
   const int64_t K = p.k;
   const int ktiles = static_cast<int>(K / BK);
@@ -137,10 +155,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
   const uint32_t a_voff = static_cast<uint32_t>((wave * 16 + a_row) * K * 2 + a_chunk * 16);
   const int b8_row = lane >> 1, b8_chunk = (lane & 1) ^ ((lane >> 4) & 1);
   const uint32_t b_voff = kInt8 ? static_cast<uint32_t>((wave * 32 + b8_row) * K + b8_chunk * 16) : a_voff;
-  const uint32_t a_step = static_cast<uint32_t>(64 * K * 2);                // 64 rows
-  const uint32_t b_step = kInt8 ? static_cast<uint32_t>(128 * K) : a_step;  // 128 int8 rows
-  constexpr int kLoadsA = Smem<kInt8>::kA / 1024 / 4;  // per thread per stage
-  constexpr int kLoadsB = Smem<kInt8>::kB / 1024 / 4;
+  const uint32_t a_step = static_cast<uint32_t>(16 * kWaves * K * 2);                 // rows per round
+  const uint32_t b_step = kInt8 ? static_cast<uint32_t>(32 * kWaves * K) : a_step;
+  constexpr int kLoadsA = Smem<kInt8>::kA / 1024 / kWaves;  // per thread per stage
+  constexpr int kLoadsB = Smem<kInt8>::kB / 1024 / kWaves;
   constexpr int kLoads = kLoadsA + kLoadsB;
 
   typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -151,27 +169,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
     const uint32_t kb = static_cast<uint32_t>(kt) * BK * (kInt8 ? 1 : 2);
 #pragma unroll
     for (int i = 0; i < kLoadsA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(sa + (4 * i + wave) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(sa + (kWaves * i + wave) * 1024), 16,
                                                a_voff + i * a_step, ka, 0, 0);
 #pragma unroll
     for (int i = 0; i < kLoadsB; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_ptr)(sb + (4 * i + wave) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_b, (lds_ptr)(sb + (kWaves * i + wave) * 1024), 16,
                                                b_voff + i * b_step, kb, 0, 0);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // Operand fragments of one 16-wide K slice: A rows of the four m-blocks, B rows of the four
+  // Operand fragments of one 16-wide K slice: A rows of the four m-blocks, B rows of the
   // n-blocks (int8 weights stay packed until just before the multiply).
   struct Frags {
     bf16x8 a[4];
-    u32x4 b[4];  // bf16: 8 values; int8: 8 codes in .xy
+    u32x4 b[NB];  // bf16: 8 values; int8: 8 codes in .xy
   };
   auto read_frags = [&](int kt, int slice, Frags& f) {
     const uint8_t* sa = smem + (kt % kStages) * Smem<kInt8>::kStage;
@@ -180,8 +198,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
     for (int mb = 0; mb < 4; ++mb)
       f.a[mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + swz16(wm * 128 + mb * 32 + li, 2 * slice + hi)));
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int row = wn * 128 + nb * 32 + li;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int row = wn * SN + nb * 32 + li;
       if constexpr (kInt8) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(sb + swz8(row, slice) + 8 * hi);
         f.b[nb] = u32x4{v.x, v.y, 0u, 0u};
@@ -191,81 +209,90 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
     }
   };
   auto mma = [&](const Frags& f) {
-    bf16x8 bv[4];
+    bf16x8 bv[NB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
       if constexpr (kInt8) bv[nb] = widen_i8(u32x2{f.b[nb].x, f.b[nb].y});
       else bv[nb] = as_bf16x8(f.b[nb]);
     }
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bv[nb], acc[mb][nb], 0, 0, 0);
   };
-  // One LDS read between consecutive MFMAs for the first half of a slice, the rest of the
-  // MFMAs back to back; kVmem buffer loads ride along with each of the first eight MFMAs.
+  // One LDS read between consecutive MFMAs until the next slice's fragments are all requested,
+  // then the remaining MFMAs back to back; kVmem buffer loads ride along with each pair.
+  constexpr int kReads = 4 + NB, kMfmas = 4 * NB;
   auto interleave = [&]<int kVmem>() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kReads; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       if constexpr (kVmem > 0) __builtin_amdgcn_sched_group_barrier(0x020, kVmem, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kReads, 0);
     __builtin_amdgcn_sched_barrier(0);  // nothing crosses: keeps each slice's MFMAs together
   };
 
-  // Four LDS stages, K step 32 (two 16-wide slices), one barrier per K step. K step kt+3
-  // streams into the stage that K step kt-1 left while kt is multiplied; the fragments of the
-  // next slice are read while the current one is multiplied. kAhead = K steps issued beyond
-  // kt+1 (2 in steady state), so waiting for vmcnt <= kAhead * kLoads leaves step kt+1 landed.
+  // kStages LDS stages, K step 32 (two 16-wide slices), one barrier per K step. K step
+  // kt+kStages-1 streams into the stage that K step kt-1 left while kt is multiplied; the
+  // fragments of the next slice are read while the current one is multiplied. kAhead = K steps
+  // in flight beyond kt+1 (kStages-2 in steady state), so waiting for vmcnt <= kAhead * kLoads
+  // leaves step kt+1 landed.
   Frags f0, f1;
   auto k_step = [&]<int kAhead>(int kt) {
     read_frags(kt, 1, f1);
-    if constexpr (kAhead == 2) issue_loads(kt + 3);
+    if constexpr (kAhead == kStages - 2) issue_loads(kt + kStages - 1);
     mma(f0);
-    interleave.template operator()<kAhead == 2 ? (kLoads + 7) / 8 : 0>();
+    interleave.template operator()<kAhead == kStages - 2 ? (kLoads + kReads - 1) / kReads : 0>();
     pipeline_barrier<(kAhead > 0 ? kAhead : 0) * kLoads>();
     if constexpr (kAhead >= 0) read_frags(kt + 1, 0, f0);
     mma(f1);
     interleave.template operator()<0>();
   };
+  // Prologue: K steps 0 .. kStages-2 in flight, wait for step 0.
   const int pre = ktiles < kStages - 1 ? ktiles : kStages - 1;
   for (int t = 0; t < pre; ++t) issue_loads(t);
-  if (pre == 3) pipeline_barrier<2 * kLoads>();
-  else if (pre == 2) pipeline_barrier<kLoads>();
-  else pipeline_barrier<0>();
+  switch (pre) {
+    case 5: pipeline_barrier<4 * kLoads>(); break;
+    case 4: pipeline_barrier<3 * kLoads>(); break;
+    case 3: pipeline_barrier<2 * kLoads>(); break;
+    case 2: pipeline_barrier<kLoads>(); break;
+    default: pipeline_barrier<0>(); break;
+  }
   read_frags(0, 0, f0);
   int kt = 0;
-  for (; kt + 3 < ktiles; ++kt) k_step.template operator()<2>(kt);
-  if (kt + 2 < ktiles) k_step.template operator()<1>(kt++);
+  for (; kt + kStages - 1 < ktiles; ++kt) k_step.template operator()<kStages - 2>(kt);
+  // Drain: fewer and fewer K steps remain in flight.
+  if constexpr (kStages - 3 >= 3) if (kt + 4 < ktiles) k_step.template operator()<3>(kt++);
+  if constexpr (kStages - 3 >= 2) if (kt + 3 < ktiles) k_step.template operator()<2>(kt++);
+  if constexpr (kStages - 3 >= 1) if (kt + 2 < ktiles) k_step.template operator()<1>(kt++);
   if (kt + 1 < ktiles) k_step.template operator()<0>(kt++);
   k_step.template operator()<-1>(kt);
 
-  // ---- epilogue through LDS. Each wave stages its 128 x 128 float32 result 32 rows at a time
-  // (row stride 136 floats: the two half-waves of an MFMA block store to disjoint banks), then
-  // reads it back row-wise (8 consecutive columns per lane: RoPE pairs and 16-byte stores) or,
-  // for the transposed v, column-wise. Element (mb, nb, 4b + r) of a lane sits at row
-  // 8b + 4hi + r of slice mb and column nb*32 + li of the wave's sub-tile.
-  constexpr int kStride = 136;
+  // ---- epilogue through LDS. Each wave stages its 128 x SN float32 result 32 rows at a time
+  // (row stride SN + 8 floats: the two half-waves of an MFMA block store to disjoint banks),
+  // then reads it back row-wise (8 consecutive columns per lane: RoPE pairs and 16-byte
+  // stores) or, for the transposed v, column-wise. Element (mb, nb, 4b + r) of a lane sits at
+  // row 8b + 4hi + r of slice mb and column nb*32 + li of the wave's sub-tile.
+  constexpr int kStride = SN + 8;
+  constexpr int kLanesRow = SN / 8;          // lanes covering one row in row-wise passes
+  constexpr int kRowsPass = 64 / kLanesRow;  // rows per row-wise instruction
   float* st = reinterpret_cast<float*>(smem) + wave * 32 * kStride;
   const int64_t row_base = m0 + wm * 128;
-  const int64_t col_base = n0 + wn * 128;
-  const int lc = (lane & 15) * 8;  // first of this lane's 8 columns in row-wise passes
+  const int64_t col_base = n0 + wn * SN;
+  const int lc = (lane % kLanesRow) * 8;  // first of this lane's 8 columns in row-wise passes
+  const int lr = lane / kLanesRow;
   float csc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) csc[j] = 1.0f;
-  if constexpr (kInt8) {
-    if constexpr (kEpi == EPI_SWIGLU) {
-      // gate and up scales of this lane's columns (see the SwiGLU pass below)
-    } else {
-      const u32x4 sraw = *reinterpret_cast<const u32x4*>(p.wscale + col_base + lc);
+  if constexpr (kInt8 && kEpi != EPI_SWIGLU) {
+    const u32x4 sraw = *reinterpret_cast<const u32x4*>(p.wscale + col_base + lc);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        csc[2 * j] = __uint_as_float(sraw[j] << 16);
-        csc[2 * j + 1] = __uint_as_float(sraw[j] & 0xffff0000u);
-      }
+    for (int j = 0; j < 4; ++j) {
+      csc[2 * j] = __uint_as_float(sraw[j] << 16);
+      csc[2 * j + 1] = __uint_as_float(sraw[j] & 0xffff0000u);
     }
   }
 
@@ -273,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
   for (int mb = 0; mb < 4; ++mb) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         st[(8 * (e >> 2) + 4 * hi + (e & 3)) * kStride + nb * 32 + li] = acc[mb][nb][e];
@@ -282,8 +309,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
 
     if constexpr (kEpi == EPI_F32 || kEpi == EPI_RESID) {
 #pragma unroll 2
-      for (int it = 0; it < 8; ++it) {
-        const int r = it * 4 + (lane >> 4);
+      for (int it = 0; it < 32 / kRowsPass; ++it) {
+        const int r = it * kRowsPass + lr;
         const int64_t row = r0 + r;
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc + 4);
@@ -313,8 +340,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
         }
       }
     } else if constexpr (kEpi == EPI_SWIGLU) {
-      // 128 packed columns = two groups of [32 gate | 32 up] -> 64 h features per row.
-      const int hc = (lane & 7) * 8;              // this lane's first h feature within the 64
+      // SN packed columns = SN/64 groups of [32 gate | 32 up] -> SN/2 h features per row.
+      constexpr int kLanesH = SN / 16, kRowsH = 64 / kLanesH;
+      const int hc = (lane % kLanesH) * 8;  // this lane's first h feature within the wave's SN/2
       const int grp = hc / 32, ih = hc % 32;
       const int gcol = grp * 64 + ih, ucol = gcol + 32;
       float sg[8], su[8];
@@ -332,8 +360,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
       const int64_t F = p.n / 2;
       const int64_t f0 = col_base / 2 + hc;
 #pragma unroll 2
-      for (int it = 0; it < 4; ++it) {
-        const int r = it * 8 + (lane >> 3);
+      for (int it = 0; it < 32 / kRowsH; ++it) {
+        const int r = it * kRowsH + lane / kLanesH;
         const int64_t row = r0 + r;
         const f32x4 ga = *reinterpret_cast<const f32x4*>(st + r * kStride + gcol);
         const f32x4 gb = *reinterpret_cast<const f32x4*>(st + r * kStride + gcol + 4);
@@ -364,8 +392,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
         const int axis = dh < ct ? 0 : (dh < ct + cy ? 1 : 2);
         const int k0 = axis == 0 ? dh / 2 : (axis == 1 ? (dh - ct) / 2 : (dh - ct - cy) / 2);
 #pragma unroll 2
-        for (int it = 0; it < 8; ++it) {
-          const int r = it * 4 + (lane >> 4);
+        for (int it = 0; it < 32 / kRowsPass; ++it) {
+          const int r = it * kRowsPass + lr;
           const int64_t row = r0 + r;
           const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc);
           const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc + 4);
@@ -401,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_kernel(GemmArgs p, int 
         // them as 64 contiguous bytes of v^T.
         uint16_t* vt = static_cast<uint16_t*>(p.vt);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int half = 0; half < SN / 64; ++half) {
           const int c = lane + 64 * half;
           const int64_t f = col_base + c - 2 * d;
           float sc = 1.0f;
@@ -508,28 +536,38 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
   }
 }
 
-template <bool kInt8>
+template <bool kInt8, int kWN>
 hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   const int tiles_m = static_cast<int>((a.m + BM - 1) / BM);
   const int tiles_n = static_cast<int>(a.n / BN);
   const int total = tiles_m * tiles_n;
   const int grid = (total + 7) / 8 * 8;
   const int group_m = 8;
+  constexpr int T = Layout<kWN>::kThreadsT;
   switch (epi) {
     case EPI_QKV:
-      gemm_mfma_kernel<kInt8, EPI_QKV><<<grid, kThreads, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_QKV, kWN><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_RESID:
-      gemm_mfma_kernel<kInt8, EPI_RESID><<<grid, kThreads, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_RESID, kWN><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_SWIGLU:
-      gemm_mfma_kernel<kInt8, EPI_SWIGLU><<<grid, kThreads, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_SWIGLU, kWN><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     default:
-      gemm_mfma_kernel<kInt8, EPI_F32><<<grid, kThreads, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_F32, kWN><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
   }
   return hipGetLastError();
+}
+
+// Wave layout of the MFMA GEMM: 4 (one 128 x 128 sub-tile per wave) or 8 (128 x 64).
+int gemm_waves() {
+  static const int w = [] {
+    const char* e = getenv("H3X_GEMM_WAVES");
+    return (e && atoi(e) == 4) ? 4 : 8;
+  }();
+  return w;
 }
 
 }  // namespace
@@ -548,8 +586,9 @@ hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& a, hipStrea
     }
     return hipGetLastError();
   }
-  return wdtype == H3X_I8 ? launch_mfma<true>(epi, a, s)
-                          : launch_mfma<false>(epi, a, s);
+  if (gemm_waves() == 4)
+    return wdtype == H3X_I8 ? launch_mfma<true, 2>(epi, a, s) : launch_mfma<false, 2>(epi, a, s);
+  return wdtype == H3X_I8 ? launch_mfma<true, 4>(epi, a, s) : launch_mfma<false, 4>(epi, a, s);
 }
 
 }  // namespace h3x
