@@ -106,11 +106,18 @@ const char *h3x_last_error(void);
 int64_t h3x_geom_tokens(const h3x_geom *geom);
 
 /* ------------------------------------------------------------------ weight packing
- * Packed layout (both element types): rows of the source are kept whole and in order, except
- * for H3X_W_GATE_UP, whose packed row 64j + i is W_gate row 32j + i and packed row
- * 64j + 32 + i is W_up row 32j + i (i < 32), so that one 64-column output group holds the gate
- * and up values of the same 32 inner features. Packed size in bytes for the cfg's weight type
- * (int8 codes for H3X_I8; scales are h3x_packed_scale_count() bfloat16 values). */
+ * Packed row order (all weight types): rows of the source are kept whole and in order, except
+ * for H3X_W_GATE_UP, whose packed row 64j + i is W_gate row 32j + i and packed row 64j + 32 + i
+ * is W_up row 32j + i (i < 32), so that one 64-column output group holds the gate and up values
+ * of the same 32 inner features.
+ * Packed storage: F32 weights are row-major [rows x cols]. BF16 weights and I8 codes are stored
+ * as slabs of 256 packed rows x 32 columns, slab (r / 256, c / 32) at byte offset
+ * ((r / 256) * (cols / 32) + c / 32) * S with S = 16384 (BF16) or 8192 (I8); inside a slab,
+ * packed row rr = r % 256 holds 64 (BF16) or 32 (I8) bytes made of 16-byte chunks, chunk q of
+ * the row stored at position q ^ ((rr >> 2) & 3) (BF16) or q ^ ((rr >> 3) & 1) (I8). This is
+ * the order in which the matrix-core GEMM keeps one 32-wide K step of a 256-row tile in LDS.
+ * Packed size in bytes for the cfg's weight type (I8: the codes; scales are
+ * h3x_packed_scale_count() bfloat16 values in packed row order). */
 size_t h3x_packed_weight_bytes(const h3x_block_cfg *cfg, int32_t kind);
 int64_t h3x_packed_rows(const h3x_block_cfg *cfg, int32_t kind);
 int64_t h3x_packed_scale_count(const h3x_block_cfg *cfg, int32_t kind);

@@ -72,3 +72,27 @@ def packed_block(w: synth.Workload, b: int):
 def modulation(w: synth.Workload, step: int, b: int):
     m = synth.modulation(w, step, b)
     return m.astype(np.float64), torch.from_numpy(m).cuda()
+
+
+def slab_byte_offsets(rows: int, cols: int, esize: int) -> np.ndarray:
+    """Byte offset of element (r, c) in the 256 x 32 slab storage stated in include/h3x.h."""
+    r = np.arange(rows, dtype=np.int64)[:, None]
+    c = np.arange(cols, dtype=np.int64)[None, :]
+    rr, cc = r & 255, c & 31
+    slab = (r >> 8) * (cols >> 5) + (c >> 5)
+    if esize == 2:
+        return (slab << 14) + rr * 64 + (((cc >> 3) ^ ((rr >> 2) & 3)) << 4) + (cc & 7) * 2
+    return (slab << 13) + rr * 32 + (((cc >> 4) ^ ((rr >> 3) & 1)) << 4) + (cc & 15)
+
+
+def unslab(t, rows: int, cols: int, esize: int) -> np.ndarray:
+    """[rows x cols] array (uint16 bf16 bits or int8) from a device tensor in slab storage."""
+    raw = t.contiguous().view(torch.uint8).reshape(-1).cpu().numpy()
+    off = slab_byte_offsets(rows, cols, esize)
+    if esize == 2:
+        return raw.view(np.uint16)[off // 2]
+    return raw.view(np.int8)[off]
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)

@@ -6,7 +6,8 @@ import torch
 import synth
 from oracle import dit, quant, sampler, tokred
 from oracle.numeric import bf16_rne
-from _util import binding_cfg, binding_geom, host, oracle_geom, rel_l2, to_dev
+from _util import (bf16_bits_to_f32, binding_cfg, binding_geom, host, oracle_geom, rel_l2, to_dev,
+                   unslab)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +47,7 @@ def test_pack_int8_bit_exact(B):
         torch.cuda.synchronize()
         qr, sr = quant.pack_int8(wb)
         perm = np.array([_src(kind, p, rows) for p in range(rows)])
-        np.testing.assert_array_equal(q.cpu().numpy(), qr[perm])
+        np.testing.assert_array_equal(unslab(q, rows, cols, 1), qr[perm])
         np.testing.assert_array_equal(s.float().cpu().numpy(), sr[perm])
 
 
@@ -66,8 +67,13 @@ def test_pack_layout_bit_exact(B, wl):
     src = synth.storage_values(gu, wl.act)
     packed = B.pack_weights(cfg, B.W_GATE_UP, to_dev(gu, wl.act))
     torch.cuda.synchronize()
-    perm = np.array([_src(2, p, gu.shape[0]) for p in range(gu.shape[0])])
-    np.testing.assert_array_equal(packed.float().cpu().numpy(), src[perm])
+    rows, cols = gu.shape
+    perm = np.array([_src(2, p, rows) for p in range(rows)])
+    if wl.act == "bf16":
+        got = bf16_bits_to_f32(unslab(packed, rows, cols, 2))
+    else:
+        got = packed.cpu().numpy()
+    np.testing.assert_array_equal(got, src[perm])
 
 
 # ---------------------------------------------------------------- modulated RMSNorm

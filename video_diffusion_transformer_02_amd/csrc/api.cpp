@@ -241,26 +241,33 @@ h3x_status block_forward_impl(const h3x_block_cfg* c, const h3x_geom* g, const h
   const float *shift1 = mod, *scale1 = mod + d, *gate1 = mod + 2 * d;
   const float *shift2 = mod + 3 * d, *scale2 = mod + 4 * d, *gate2 = mod + 5 * d;
 
-  H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n, c->d_model, c->norm_eps, x, shift1, scale1, ws.y, s));
+  // bf16: the GEMM A operands (y, o, y2, h) live in the slab layout of the MFMA GEMM.
+  const int tiled = c->act == H3X_BF16 ? 1 : 0;
+  H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n, c->d_model, c->norm_eps, x, shift1, scale1, ws.y, tiled, s));
 
   GemmArgs qa = gemm_args(c, H3X_W_QKV, n, ws.y, w->qkv, w->s_qkv);
+  qa.a_tiled = tiled;
   qa.m_pad = ws.n_pad;
   qa.q = ws.q; qa.kk = ws.k; qa.vt = ws.vt; qa.geom = gd; qa.rope = rd;
   H3X_LAUNCH(gemm_name(EPI_QKV), s, launch_gemm(c->act, c->weight, EPI_QKV, qa, s));
 
-  H3X_LAUNCH("attention", s, launch_attention(c->act, n, ws.n_pad, c->n_heads, c->head_dim, ws.q, ws.k, ws.vt, ws.o, s));
+  H3X_LAUNCH("attention", s, launch_attention(c->act, n, ws.n_pad, c->n_heads, c->head_dim, ws.q, ws.k, ws.vt, ws.o, tiled, s));
 
   GemmArgs oa = gemm_args(c, H3X_W_OUT, n, ws.o, w->out, w->s_out);
+  oa.a_tiled = tiled;
   oa.x = x; oa.gate = gate1;
   H3X_LAUNCH("gemm_out_resid", s, launch_gemm(c->act, c->weight, EPI_RESID, oa, s));
 
-  H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n, c->d_model, c->norm_eps, x, shift2, scale2, ws.y, s));
+  H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n, c->d_model, c->norm_eps, x, shift2, scale2, ws.y, tiled, s));
 
   GemmArgs ga = gemm_args(c, H3X_W_GATE_UP, n, ws.y, w->gate_up, w->s_gate_up);
+  ga.a_tiled = tiled;
+  ga.out_tiled = tiled;
   ga.h = ws.h;
   H3X_LAUNCH(gemm_name(EPI_SWIGLU), s, launch_gemm(c->act, c->weight, EPI_SWIGLU, ga, s));
 
   GemmArgs da = gemm_args(c, H3X_W_DOWN, n, ws.h, w->down, w->s_down);
+  da.a_tiled = tiled;
   da.x = x; da.gate = gate2;
   H3X_LAUNCH("gemm_down_resid", s, launch_gemm(c->act, c->weight, EPI_RESID, da, s));
   return H3X_OK;
@@ -488,7 +495,7 @@ h3x_status h3x_norm_mod(const h3x_block_cfg* c, int64_t n_rows, const void* x, c
   if (!x || !shift || !scale || !y || !aligned16(x) || !aligned16(y) || !aligned16(shift) || !aligned16(scale))
     return fail(H3X_EINVAL, "norm_mod: NULL or misaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n_rows, c->d_model, c->norm_eps, x, shift, scale, y, s));
+  H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n_rows, c->d_model, c->norm_eps, x, shift, scale, y, 0, s));
   return H3X_OK;
 }
 
@@ -532,7 +539,7 @@ h3x_status h3x_attention(const h3x_block_cfg* c, int64_t n_tokens, const void* q
   if (!q || !k || !vt || !o || !aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
     return fail(H3X_EINVAL, "attention: NULL or misaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  H3X_LAUNCH("attention", s, launch_attention(c->act, n_tokens, round_up(n_tokens, 256), c->n_heads, c->head_dim, q, k, vt, o, s));
+  H3X_LAUNCH("attention", s, launch_attention(c->act, n_tokens, round_up(n_tokens, 256), c->n_heads, c->head_dim, q, k, vt, o, 0, s));
   return H3X_OK;
 }
 

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
                                                                  const uint16_t* __restrict__ vt,
                                                                  uint16_t* __restrict__ o,
                                                                  int n, int n_pad, int n_heads,
-                                                                 int qblocks) {
+                                                                 int qblocks, int o_tiled) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
 
   const int total = n_heads * qblocks;
@@ -193,7 +193,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
                             (static_cast<uint32_t>(f32_to_bf16_bits(oacc[db][4 * b + 1] * inv)) << 16);
         const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(oacc[db][4 * b + 2] * inv)) |
                             (static_cast<uint32_t>(f32_to_bf16_bits(oacc[db][4 * b + 3] * inv)) << 16);
-        *reinterpret_cast<u32x2*>(op + dim) = u32x2{w0, w1};
+        if (o_tiled)  // 256-row x 32-column slabs (slab_offset); 4 dims stay inside one chunk
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(o) + slab_offset(qrow, head * kDh + dim, d)) = u32x2{w0, w1};
+        else
+          *reinterpret_cast<u32x2*>(op + dim) = u32x2{w0, w1};
       }
   }
 }
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 }  // namespace
 
 hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_heads, int head_dim,
-                            const void* q, const void* k, const void* vt, void* o,
+                            const void* q, const void* k, const void* vt, void* o, int o_tiled,
                             hipStream_t s) {
   if (n_tokens == 0) return hipSuccess;
   const int n = static_cast<int>(n_tokens), np = static_cast<int>(n_pad);
@@ -250,7 +253,7 @@ hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_head
     attn_mfma_kernel<<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(q),
                                                static_cast<const uint16_t*>(k),
                                                static_cast<const uint16_t*>(vt),
-                                               static_cast<uint16_t*>(o), n, np, n_heads, qblocks);
+                                               static_cast<uint16_t*>(o), n, np, n_heads, qblocks, o_tiled);
   } else {
     dim3 grid(static_cast<unsigned>((n + 63) / 64), static_cast<unsigned>(n_heads));
     if (head_dim == 64)

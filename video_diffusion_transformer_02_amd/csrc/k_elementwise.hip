@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void norm_mod_kernel(const typename E::T*
                                                             const float* __restrict__ shift,
                                                             const float* __restrict__ scale,
                                                             typename E::T* __restrict__ y,
-                                                            int d, float eps) {
+                                                            int d, float eps, int out_tiled) {
   constexpr int V = Vec<E>::n;
   __shared__ float part[kThreads / 64];
   const int64_t row = blockIdx.x;
@@ -88,7 +88,10 @@ __global__ __launch_bounds__(kThreads) void norm_mod_kernel(const typename E::T*
       v[4 * j + 2] = fmaf(v[4 * j + 2] * r, 1.f + sc.z, sh.z);
       v[4 * j + 3] = fmaf(v[4 * j + 3] * r, 1.f + sc.w, sh.w);
     }
-    store16<E>(yr + i, v);
+    if (out_tiled)  // bf16 only: 256-row x 32-column slabs (see slab_offset)
+      store16<E>(reinterpret_cast<typename E::T*>(reinterpret_cast<uint8_t*>(y) + slab_offset(row, i, d)), v);
+    else
+      store16<E>(yr + i, v);
   }
 }
 
@@ -238,6 +241,8 @@ __global__ void rope_rowbase_kernel(int4* __restrict__ rowbase, GeomDev g, int k
 }
 
 // ---------------------------------------------------------------- weight packing
+// float32 weights: packed rows stay row-major. bfloat16 weights: packed rows are stored as
+// 256-row x 32-column slabs (slab_offset), the operand order of the MFMA GEMM.
 template <class T>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const T* __restrict__ w,
                                                         T* __restrict__ packed, int kind,
@@ -249,12 +254,14 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const T* __restrict__ w,
        idx += (int64_t)gridDim.x * kThreads) {
     const int64_t p = idx / cpr, c = (idx % cpr) * V;
     const int64_t src = packed_source_row(kind, p, rows);
-    *reinterpret_cast<uint4*>(packed + p * cols + c) =
-        *reinterpret_cast<const uint4*>(w + src * cols + c);
+    T* dst = sizeof(T) == 2 ? reinterpret_cast<T*>(reinterpret_cast<uint8_t*>(packed) + slab_offset(p, c, cols))
+                            : packed + p * cols + c;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(w + src * cols + c);
   }
 }
 
 // One workgroup per packed row: amax, scale = bf16(amax / 127), codes = clamp(rint(w / s)).
+// Codes are stored as 256-row x 32-byte slabs (slab_offset_i8); scales in packed row order.
 __global__ __launch_bounds__(kThreads) void pack_int8_kernel(const uint16_t* __restrict__ w,
                                                              int8_t* __restrict__ q,
                                                              uint16_t* __restrict__ scale,
@@ -280,7 +287,6 @@ __global__ __launch_bounds__(kThreads) void pack_int8_kernel(const uint16_t* __r
   const uint16_t sbits = a == 0.f ? 0 : f32_to_bf16_bits(a / 127.0f);
   const float s = bf16_bits_to_f32(sbits);
   if (threadIdx.x == 0) scale[p] = sbits;
-  int8_t* qr = q + p * cols;
   for (int64_t c = threadIdx.x * 8; c < cols; c += kThreads * 8) {
     float v[8];
     load16<BF16>(wr + c, v);
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void pack_int8_kernel(const uint16_t* __r
       const uint32_t b = static_cast<uint32_t>(qi) & 0xffu;
       if (j < 4) lo |= b << (8 * j); else hi |= b << (8 * (j - 4));
     }
-    *reinterpret_cast<uint2*>(qr + c) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(q + slab_offset_i8(p, c, cols)) = make_uint2(lo, hi);
   }
 }
 
@@ -306,14 +312,15 @@ int grid_for(int64_t work_items) {
 }  // namespace
 
 hipError_t launch_norm_mod(int act, int64_t n_rows, int d, float eps, const void* x,
-                           const float* shift, const float* scale, void* y, hipStream_t s) {
+                           const float* shift, const float* scale, void* y, int out_tiled,
+                           hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
   if (act == H3X_BF16)
     norm_mod_kernel<BF16><<<dim3(n_rows), kThreads, 0, s>>>(
-        static_cast<const uint16_t*>(x), shift, scale, static_cast<uint16_t*>(y), d, eps);
+        static_cast<const uint16_t*>(x), shift, scale, static_cast<uint16_t*>(y), d, eps, out_tiled);
   else
     norm_mod_kernel<F32><<<dim3(n_rows), kThreads, 0, s>>>(
-        static_cast<const float*>(x), shift, scale, static_cast<float*>(y), d, eps);
+        static_cast<const float*>(x), shift, scale, static_cast<float*>(y), d, eps, 0);
   return hipGetLastError();
 }
 

@@ -111,7 +111,7 @@ struct Layout {
   static constexpr int NB = SN / 32;   // 32-wide MFMA blocks per wave along N
 };
 
-template <bool kInt8, int kEpi, int kWN>
+template <bool kInt8, int kEpi, int kWN, bool kATiled>
 __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(GemmArgs p, int tiles_m,
                                                                                 int tiles_n, int group_m) {
   using L = Layout<kWN>;
@@ -140,23 +140,27 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   const int ktiles = static_cast<int>(K / BK);
 
   // ---- global -> LDS without registers: buffer_load_dwordx4 ... lds writes lane l's 16 bytes
-  // at (wave-uniform base) + 16 l. One wave instruction fills 1 KB of a stage: 16 bf16 rows of
-  // 64 bytes, or 32 int8 rows of 32 bytes; each lane fetches the global chunk that the swizzle
-  // places at its LDS position. Rows past the end of A lie outside the buffer's range and read
-  // as zeros.
-  const uint8_t* Ab = static_cast<const uint8_t*>(p.a) + m0 * K * 2;
-  const uint8_t* Wb = static_cast<const uint8_t*>(p.w) + n0 * K * (kInt8 ? 1 : 2);
+  // at (wave-uniform base) + 16 l, so one wave instruction fills 1 KB of a stage.
+  //  * Packed weights and tiled activations are stored as 256-row x 32-column slabs already in
+  //    the LDS order (see slab_offset), so a K step of an operand is one contiguous 16 KB (bf16)
+  //    or 8 KB (int8) run that the lanes copy linearly.
+  //  * Row-major A (the kernel-level entry points): each lane fetches the 16-byte chunk that the
+  //    swizzle places at its LDS position; rows past the end of A lie outside the buffer's range
+  //    and read as zeros.
+  constexpr int kSlabA = BM * BK * 2, kSlabB = BN * BK * (kInt8 ? 1 : 2);
+  const uint8_t* Ab = static_cast<const uint8_t*>(p.a) + (kATiled ? tm * (K / BK) * kSlabA : m0 * K * 2);
+  const uint8_t* Wb = static_cast<const uint8_t*>(p.w) + tn * (K / BK) * kSlabB;
   const int64_t a_rows = p.m - m0 < BM ? p.m - m0 : BM;
   const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(Ab), 0, static_cast<int>(a_rows * K * 2), 0x00020000);
+      const_cast<uint8_t*>(Ab), 0, static_cast<int>(kATiled ? (K / BK) * kSlabA : a_rows * K * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(Wb), 0, static_cast<int>(BN * K * (kInt8 ? 1 : 2)), 0x00020000);
+      const_cast<uint8_t*>(Wb), 0, static_cast<int>((K / BK) * kSlabB), 0x00020000);
+  const uint32_t lin_voff = static_cast<uint32_t>(wave * 1024 + lane * 16);
+  const uint32_t lin_step = static_cast<uint32_t>(kWaves * 1024);
   const int a_row = lane >> 2, a_chunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const uint32_t a_voff = static_cast<uint32_t>((wave * 16 + a_row) * K * 2 + a_chunk * 16);
-  const int b8_row = lane >> 1, b8_chunk = (lane & 1) ^ ((lane >> 4) & 1);
-  const uint32_t b_voff = kInt8 ? static_cast<uint32_t>((wave * 32 + b8_row) * K + b8_chunk * 16) : a_voff;
-  const uint32_t a_step = static_cast<uint32_t>(16 * kWaves * K * 2);                 // rows per round
-  const uint32_t b_step = kInt8 ? static_cast<uint32_t>(32 * kWaves * K) : a_step;
+  const uint32_t a_voff = kATiled ? lin_voff : static_cast<uint32_t>((wave * 16 + a_row) * K * 2 + a_chunk * 16);
+  const uint32_t a_step = kATiled ? lin_step : static_cast<uint32_t>(16 * kWaves * K * 2);
+  const uint32_t b_voff = lin_voff, b_step = lin_step;
   constexpr int kLoadsA = Smem<kInt8>::kA / 1024 / kWaves;  // per thread per stage
   constexpr int kLoadsB = Smem<kInt8>::kB / 1024 / kWaves;
   constexpr int kLoads = kLoadsA + kLoadsB;
@@ -165,8 +169,8 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   auto issue_loads = [&](int kt) {
     uint8_t* sa = smem + (kt % kStages) * Smem<kInt8>::kStage;
     uint8_t* sb = sa + Smem<kInt8>::kA;
-    const uint32_t ka = static_cast<uint32_t>(kt) * BK * 2;
-    const uint32_t kb = static_cast<uint32_t>(kt) * BK * (kInt8 ? 1 : 2);
+    const uint32_t ka = static_cast<uint32_t>(kt) * (kATiled ? kSlabA : BK * 2);
+    const uint32_t kb = static_cast<uint32_t>(kt) * kSlabB;
 #pragma unroll
     for (int i = 0; i < kLoadsA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_ptr)(sa + (kWaves * i + wave) * 1024), 16,
@@ -378,7 +382,10 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
             out[j] = static_cast<uint32_t>(f32_to_bf16_bits(h0)) |
                      (static_cast<uint32_t>(f32_to_bf16_bits(h1)) << 16);
           }
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.h) + row * F + f0) = out;
+          if (p.out_tiled)
+            *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.h) + slab_offset(row, f0, F)) = out;
+          else
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.h) + row * F + f0) = out;
         }
       }
     } else {  // EPI_QKV
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
   }
 }
 
-template <bool kInt8, int kWN>
+template <bool kInt8, int kWN, bool kATiled>
 hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   const int tiles_m = static_cast<int>((a.m + BM - 1) / BM);
   const int tiles_n = static_cast<int>(a.n / BN);
@@ -546,16 +553,16 @@ hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   constexpr int T = Layout<kWN>::kThreadsT;
   switch (epi) {
     case EPI_QKV:
-      gemm_mfma_kernel<kInt8, EPI_QKV, kWN><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_QKV, kWN, kATiled><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_RESID:
-      gemm_mfma_kernel<kInt8, EPI_RESID, kWN><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_RESID, kWN, kATiled><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_SWIGLU:
-      gemm_mfma_kernel<kInt8, EPI_SWIGLU, kWN><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_SWIGLU, kWN, kATiled><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     default:
-      gemm_mfma_kernel<kInt8, EPI_F32, kWN><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_F32, kWN, kATiled><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
   }
   return hipGetLastError();
@@ -586,9 +593,13 @@ hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& a, hipStrea
     }
     return hipGetLastError();
   }
-  if (gemm_waves() == 4)
-    return wdtype == H3X_I8 ? launch_mfma<true, 2>(epi, a, s) : launch_mfma<false, 2>(epi, a, s);
-  return wdtype == H3X_I8 ? launch_mfma<true, 4>(epi, a, s) : launch_mfma<false, 4>(epi, a, s);
+  const bool i8 = wdtype == H3X_I8;
+  if (gemm_waves() == 4) {
+    if (a.a_tiled) return i8 ? launch_mfma<true, 2, true>(epi, a, s) : launch_mfma<false, 2, true>(epi, a, s);
+    return i8 ? launch_mfma<true, 2, false>(epi, a, s) : launch_mfma<false, 2, false>(epi, a, s);
+  }
+  if (a.a_tiled) return i8 ? launch_mfma<true, 4, true>(epi, a, s) : launch_mfma<false, 4, true>(epi, a, s);
+  return i8 ? launch_mfma<true, 4, false>(epi, a, s) : launch_mfma<false, 4, false>(epi, a, s);
 }
 
 }  // namespace h3x

@@ -8,7 +8,8 @@ namespace h3x {
 
 // Elementwise and memory-bound kernels (k_elementwise.hip).
 hipError_t launch_norm_mod(int act, int64_t n_rows, int d, float eps, const void* x,
-                           const float* shift, const float* scale, void* y, hipStream_t s);
+                           const float* shift, const float* scale, void* y, int out_tiled,
+                           hipStream_t s);
 hipError_t launch_token_merge(int act, const GeomDev& g, int d, const void* x, void* xm,
                               hipStream_t s);
 hipError_t launch_token_unmerge(int act, const GeomDev& g, int d, const void* xm, void* x,
@@ -24,6 +25,24 @@ hipError_t launch_pack(int wdtype, int kind, int64_t rows, int64_t cols, const v
                        void* packed, hipStream_t s);
 hipError_t launch_pack_int8(int kind, int64_t rows, int64_t cols, const void* w_bf16,
                             int8_t* q, uint16_t* scale, hipStream_t s);
+
+// Byte offset of bf16 element (r, c) of a [rows x k] matrix stored as 256-row x 32-column slabs:
+// slab (r / 256, c / 32) at ((r / 256) * (k / 32) + c / 32) * 16 KB; inside it, row rr = r % 256
+// holds 64 bytes whose four 16-byte chunks are permuted by chunk ^ ((rr >> 2) & 3). This is the
+// order in which the MFMA GEMM keeps an operand K step in LDS, so one K step of one 256-row tile
+// is a contiguous copy. k must be a multiple of 32.
+__host__ __device__ inline int64_t slab_offset(int64_t r, int64_t c, int64_t k) {
+  const int64_t rr = r & 255, cc = c & 31;
+  return (((r >> 8) * (k >> 5) + (c >> 5)) << 14) + rr * 64 + ((((cc >> 3) ^ ((rr >> 2) & 3))) << 4) +
+         (cc & 7) * 2;
+}
+// Same for int8 codes: 256 x 32-byte slabs of 8 KB, two 16-byte chunks per row permuted by
+// chunk ^ ((rr >> 3) & 1).
+__host__ __device__ inline int64_t slab_offset_i8(int64_t r, int64_t c, int64_t k) {
+  const int64_t rr = r & 255, cc = c & 31;
+  return (((r >> 8) * (k >> 5) + (c >> 5)) << 13) + rr * 32 + ((((cc >> 4) ^ ((rr >> 3) & 1))) << 4) +
+         (cc & 15);
+}
 
 // Source row of packed row p (the gate/up interleave; identity for the other kinds).
 __host__ __device__ inline int64_t packed_source_row(int kind, int64_t p, int64_t rows) {
@@ -42,7 +61,9 @@ enum Epi : int {
 };
 
 struct GemmArgs {
-  const void* a;        // [m x k] act type, row-major
+  const void* a;        // [m x k] act type: row-major, or slabs (a_tiled) as slab_offset()
+  int a_tiled;          // bf16 MFMA path only
+  int out_tiled;        // EPI_SWIGLU: h written as slabs instead of row-major
   const void* w;        // packed weight [n x k] (bf16, f32 or int8 codes)
   const uint16_t* wscale;  // int8 scales [n] (bfloat16) or nullptr
   int64_t m, n, k;
@@ -62,7 +83,7 @@ struct GemmArgs {
 
 hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& args, hipStream_t s);
 hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_heads, int head_dim,
-                            const void* q, const void* k, const void* vt, void* o,
+                            const void* q, const void* k, const void* vt, void* o, int o_tiled,
                             hipStream_t s);
 
 }  // namespace h3x
