@@ -29,10 +29,14 @@ constexpr int kStage = kTileK + kTileV;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// K tile: [64 keys][128 dims] = 16 chunks of 16 bytes per row, chunk index ^ (row & 15).
+// K tile: [64 keys][128 dims] = 16 chunks of 16 bytes per row, chunk index ^ (row & 15). Rows
+// are 256 bytes (a full bank cycle), so 8 consecutive rows read at one chunk hit 8 distinct
+// 16-byte bank groups.
 __device__ __forceinline__ int k_off(int row, int c) { return row * 256 + ((c ^ (row & 15)) << 4); }
-// V^T tile: [128 dims][64 keys] = 8 chunks per row, chunk index ^ (row & 7).
-__device__ __forceinline__ int v_off(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+// V^T tile: [128 dims][64 keys] = 8 chunks per 128-byte row, chunk index ^ ((row >> 1) & 7):
+// the 8-byte reads of 16 consecutive rows (even rows in one half of the banks, odd rows in the
+// other) then fall on 16 distinct bank pairs.
+__device__ __forceinline__ int v_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ k,
@@ -63,29 +67,35 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
     for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s));
   }
 
-  const uint16_t* kbase = k + head * kDh;
-  const uint16_t* vbase = vt + static_cast<int64_t>(head) * kDh * n_pad;
-  u32x4 rk[4], rv[4];
-  auto load_tile = [&](int kb) {
-    const int64_t key0 = static_cast<int64_t>(kb) * kBK;
+  // K and V^T tiles stream straight into LDS (buffer_load_dwordx4 ... lds: lane l's 16 bytes
+  // land at the wave's 1 KB piece + 16 l); each lane fetches the chunk that the swizzle places
+  // at its LDS position.
+  const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(k), 0, static_cast<int>(static_cast<int64_t>(n_pad) * d * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vt), 0, static_cast<int>(static_cast<int64_t>(n_pad) * d * 2), 0x00020000);
+  uint32_t k_voff[4], v_voff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 4) + 16 * i;  // key
-      rk[i] = *reinterpret_cast<const u32x4*>(kbase + (key0 + row) * d + (tid & 15) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 32 * i;  // dim
-      rv[i] = *reinterpret_cast<const u32x4*>(vbase + row * static_cast<int64_t>(n_pad) + key0 + (tid & 7) * 8);
-    }
-  };
-  auto store_tile = [&](int stage) {
-    uint8_t* sk = smem + stage * kStage;
+  for (int i = 0; i < 4; ++i) {
+    const int kr = 4 * (4 * i + wave) + (lane >> 4);          // key row of the K tile
+    const int kc = (lane & 15) ^ (kr & 15);
+    k_voff[i] = static_cast<uint32_t>((kr * d + head * kDh + kc * 8) * 2);
+    const int vr = 8 * (4 * i + wave) + (lane >> 3);          // dim row of the V^T tile
+    const int vc = (lane & 7) ^ ((vr >> 1) & 7);
+    v_voff[i] = static_cast<uint32_t>(((static_cast<int64_t>(head) * kDh + vr) * n_pad + vc * 8) * 2);
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto issue_tile = [&](int kb) {
+    uint8_t* sk = smem + (kb & 1) * kStage;
     uint8_t* sv = sk + kTileK;
+    const uint32_t ko = static_cast<uint32_t>(kb) * kBK * static_cast<uint32_t>(d) * 2;
+    const uint32_t vo = static_cast<uint32_t>(kb) * kBK * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sk + k_off((tid >> 4) + 16 * i, tid & 15)) = rk[i];
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_k, (lds_ptr)(sk + (4 * i + wave) * 1024), 16, k_voff[i], ko, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sv + v_off((tid >> 3) + 32 * i, tid & 7)) = rv[i];
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (lds_ptr)(sv + (4 * i + wave) * 1024), 16, v_voff[i], vo, 0, 0);
   };
 
   f32x16 oacc[4];
@@ -93,18 +103,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // running max in base-2 exponent units, partial sum
   const float c = 1.4426950408889634f / sqrtf(static_cast<float>(kDh));
 
   const int ktiles = (n + kBK - 1) / kBK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  issue_tile(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   for (int kb = 0; kb < ktiles; ++kb) {
-    const int stage = kb & 1;
-    if (kb + 1 < ktiles) load_tile(kb + 1);
-    const uint8_t* sk = smem + stage * kStage;
+    if (kb + 1 < ktiles) issue_tile(kb + 1);
+    const uint8_t* sk = smem + (kb & 1) * kStage;
     const uint8_t* sv = sk + kTileK;
 
     // S^T for keys kb*64 + 32*kh + (8b + 4hi + r), query qrow.
@@ -120,23 +128,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
       }
     }
 
-    // Online softmax in base-2 units.
+    // Online softmax: the running max is kept in base-2 units; the score scale is folded into
+    // the exponent's fused multiply-add.
     float mx = -INFINITY;
-    const bool tail = (kb + 1) * kBK > n;
+    if ((kb + 1) * kBK > n) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb * kBK + 32 * kh + 8 * (e >> 2) + 4 * hi + (e & 3);
+          if (key >= n) sacc[kh][e] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float t = sacc[kh][e] * c;
-        if (tail) {
-          const int key = kb * kBK + 32 * kh + 8 * (e >> 2) + 4 * hi + (e & 3);
-          if (key >= n) t = -INFINITY;
-        }
-        sacc[kh][e] = t;
-        mx = fmaxf(mx, t);
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kh][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx * c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
@@ -144,15 +153,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[kh][e] - m_new);
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kh][e], c, -m_new));
         sacc[kh][e] = pv;
         psum += pv;
       }
     l_run = fmaf(l_run, alpha, psum);
+    if (__ballot(alpha != 1.0f)) {  // the max moved for some query of this wave
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+    }
 
     // P^T fragments: for 16-key group j, element e is key 16j + 8(e/4) + 4hi + e%4.
     bf16x8 pf[4];
@@ -176,8 +187,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[db], 0, 0, 0);
       }
 
-    if (kb + 1 < ktiles) store_tile(stage ^ 1);
-    __syncthreads();
+    // Tile kb+1 has landed (own loads) and every wave is done with tile kb's stage.
+    if (kb + 1 < ktiles) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   const float l = l_run + __shfl_xor(l_run, 32, 64);
