@@ -16,6 +16,7 @@
 // gated residual (x += gate * acc), SwiGLU over the 32-row gate/up interleave, float32 store.
 #include <math.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "launch.h"
 
@@ -111,7 +112,7 @@ struct Layout {
   static constexpr int NB = SN / 32;   // 32-wide MFMA blocks per wave along N
 };
 
-template <bool kInt8, int kEpi, int kWN, bool kATiled>
+template <bool kInt8, int kEpi, int kWN, bool kATiled, bool kPingPong = false>
 __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(GemmArgs p, int tiles_m,
                                                                                 int tiles_n, int group_m) {
   using L = Layout<kWN>;
@@ -239,41 +240,82 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
     __builtin_amdgcn_sched_barrier(0);  // nothing crosses: keeps each slice's MFMAs together
   };
 
-  // kStages LDS stages, K step 32 (two 16-wide slices), one barrier per K step. K step
-  // kt+kStages-1 streams into the stage that K step kt-1 left while kt is multiplied; the
-  // fragments of the next slice are read while the current one is multiplied. kAhead = K steps
-  // in flight beyond kt+1 (kStages-2 in steady state), so waiting for vmcnt <= kAhead * kLoads
-  // leaves step kt+1 landed.
-  Frags f0, f1;
-  auto k_step = [&]<int kAhead>(int kt) {
-    read_frags(kt, 1, f1);
-    if constexpr (kAhead == kStages - 2) issue_loads(kt + kStages - 1);
-    mma(f0);
-    interleave.template operator()<kAhead == kStages - 2 ? (kLoads + kReads - 1) / kReads : 0>();
-    pipeline_barrier<(kAhead > 0 ? kAhead : 0) * kLoads>();
-    if constexpr (kAhead >= 0) read_frags(kt + 1, 0, f0);
-    mma(f1);
-    interleave.template operator()<0>();
-  };
-  // Prologue: K steps 0 .. kStages-2 in flight, wait for step 0.
-  const int pre = ktiles < kStages - 1 ? ktiles : kStages - 1;
-  for (int t = 0; t < pre; ++t) issue_loads(t);
-  switch (pre) {
-    case 5: pipeline_barrier<4 * kLoads>(); break;
-    case 4: pipeline_barrier<3 * kLoads>(); break;
-    case 3: pipeline_barrier<2 * kLoads>(); break;
-    case 2: pipeline_barrier<kLoads>(); break;
-    default: pipeline_barrier<0>(); break;
+  if constexpr (kPingPong) {
+    // Ping-pong schedule (eight waves, two per SIMD): waves 0-3 and 4-7 alternate between a
+    // memory phase (stream a future K step into LDS, read this K step's fragments) and a
+    // compute phase (its 16 MFMAs), offset by one barrier interval, so that on every SIMD one
+    // wave feeds the matrix core while the other one loads. Every interval ends with a
+    // workgroup barrier at which each wave has at most kStages-2 of its K-step loads in
+    // flight: the step read next has landed, and the stage written next has been read by both
+    // groups in earlier intervals.
+    Frags fa, fb;
+    const int group = wave / kWN;
+    auto barrier_main = [&]() { pipeline_barrier<(kStages - 2) * kLoads>(); };
+    auto barrier_drain = [&]() { pipeline_barrier<0>(); };
+    auto compute = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+      mma(fa);
+      mma(fb);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    const int pre = ktiles < kStages - 1 ? ktiles : kStages - 1;
+    for (int t = 0; t < pre; ++t) issue_loads(t);
+    if (pre == kStages - 1) barrier_main(); else barrier_drain();
+    if (group == 1) barrier_main();  // group 1 runs one interval behind
+    int kt = 0;
+    for (; kt + kStages - 1 < ktiles; ++kt) {
+      read_frags(kt, 0, fa);
+      read_frags(kt, 1, fb);
+      issue_loads(kt + kStages - 1);
+      barrier_main();
+      compute();
+      barrier_main();
+    }
+    for (; kt < ktiles; ++kt) {
+      read_frags(kt, 0, fa);
+      read_frags(kt, 1, fb);
+      barrier_drain();
+      compute();
+      barrier_drain();
+    }
+    if (group == 0) barrier_drain();  // same number of barriers in both groups
+  } else {
+    // kStages LDS stages, K step 32 (two 16-wide slices), one barrier per K step. K step
+    // kt+kStages-1 streams into the stage that K step kt-1 left while kt is multiplied; the
+    // fragments of the next slice are read while the current one is multiplied. kAhead = K steps
+    // in flight beyond kt+1 (kStages-2 in steady state), so waiting for vmcnt <= kAhead * kLoads
+    // leaves step kt+1 landed.
+    Frags f0, f1;
+    auto k_step = [&]<int kAhead>(int kt) {
+      read_frags(kt, 1, f1);
+      if constexpr (kAhead == kStages - 2) issue_loads(kt + kStages - 1);
+      mma(f0);
+      interleave.template operator()<kAhead == kStages - 2 ? (kLoads + kReads - 1) / kReads : 0>();
+      pipeline_barrier<(kAhead > 0 ? kAhead : 0) * kLoads>();
+      if constexpr (kAhead >= 0) read_frags(kt + 1, 0, f0);
+      mma(f1);
+      interleave.template operator()<0>();
+    };
+    // Prologue: K steps 0 .. kStages-2 in flight, wait for step 0.
+    const int pre = ktiles < kStages - 1 ? ktiles : kStages - 1;
+    for (int t = 0; t < pre; ++t) issue_loads(t);
+    switch (pre) {
+      case 5: pipeline_barrier<4 * kLoads>(); break;
+      case 4: pipeline_barrier<3 * kLoads>(); break;
+      case 3: pipeline_barrier<2 * kLoads>(); break;
+      case 2: pipeline_barrier<kLoads>(); break;
+      default: pipeline_barrier<0>(); break;
+    }
+    read_frags(0, 0, f0);
+    int kt = 0;
+    for (; kt + kStages - 1 < ktiles; ++kt) k_step.template operator()<kStages - 2>(kt);
+    // Drain: fewer and fewer K steps remain in flight.
+    if constexpr (kStages - 3 >= 3) if (kt + 4 < ktiles) k_step.template operator()<3>(kt++);
+    if constexpr (kStages - 3 >= 2) if (kt + 3 < ktiles) k_step.template operator()<2>(kt++);
+    if constexpr (kStages - 3 >= 1) if (kt + 2 < ktiles) k_step.template operator()<1>(kt++);
+    if (kt + 1 < ktiles) k_step.template operator()<0>(kt++);
+    k_step.template operator()<-1>(kt);
   }
-  read_frags(0, 0, f0);
-  int kt = 0;
-  for (; kt + kStages - 1 < ktiles; ++kt) k_step.template operator()<kStages - 2>(kt);
-  // Drain: fewer and fewer K steps remain in flight.
-  if constexpr (kStages - 3 >= 3) if (kt + 4 < ktiles) k_step.template operator()<3>(kt++);
-  if constexpr (kStages - 3 >= 2) if (kt + 3 < ktiles) k_step.template operator()<2>(kt++);
-  if constexpr (kStages - 3 >= 1) if (kt + 2 < ktiles) k_step.template operator()<1>(kt++);
-  if (kt + 1 < ktiles) k_step.template operator()<0>(kt++);
-  k_step.template operator()<-1>(kt);
 
   // ---- epilogue through LDS. Each wave stages its 128 x SN float32 result 32 rows at a time
   // (row stride SN + 8 floats: the two half-waves of an MFMA block store to disjoint banks),
@@ -543,7 +585,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
   }
 }
 
-template <bool kInt8, int kWN, bool kATiled>
+template <bool kInt8, int kWN, bool kATiled, bool kPP>
 hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   const int tiles_m = static_cast<int>((a.m + BM - 1) / BM);
   const int tiles_n = static_cast<int>(a.n / BN);
@@ -553,28 +595,41 @@ hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   constexpr int T = Layout<kWN>::kThreadsT;
   switch (epi) {
     case EPI_QKV:
-      gemm_mfma_kernel<kInt8, EPI_QKV, kWN, kATiled><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_QKV, kWN, kATiled, kPP><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_RESID:
-      gemm_mfma_kernel<kInt8, EPI_RESID, kWN, kATiled><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_RESID, kWN, kATiled, kPP><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_SWIGLU:
-      gemm_mfma_kernel<kInt8, EPI_SWIGLU, kWN, kATiled><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_SWIGLU, kWN, kATiled, kPP><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     default:
-      gemm_mfma_kernel<kInt8, EPI_F32, kWN, kATiled><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_F32, kWN, kATiled, kPP><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
   }
   return hipGetLastError();
 }
 
-// Wave layout of the MFMA GEMM: 4 (one 128 x 128 sub-tile per wave) or 8 (128 x 64).
-int gemm_waves() {
-  static const int w = [] {
-    const char* e = getenv("H3X_GEMM_WAVES");
-    return (e && atoi(e) == 4) ? 4 : 8;
+// Schedule of the MFMA GEMM: 4 waves (one 128 x 128 sub-tile each), 8 waves (128 x 64 each,
+// both halves in step), or 8 waves in ping-pong (the default).
+enum GemmMode { kMode4 = 0, kMode8 = 1, kModePP = 2 };
+int gemm_mode() {
+  static const int m = [] {
+    const char* e = getenv("H3X_GEMM_MODE");
+    if (e && strcmp(e, "w4") == 0) return static_cast<int>(kMode4);
+    if (e && strcmp(e, "w8") == 0) return static_cast<int>(kMode8);
+    return static_cast<int>(kModePP);
   }();
-  return w;
+  return m;
+}
+
+template <bool kInt8, bool kATiled>
+hipError_t launch_mode(int epi, const GemmArgs& a, hipStream_t s) {
+  switch (gemm_mode()) {
+    case kMode4: return launch_mfma<kInt8, 2, kATiled, false>(epi, a, s);
+    case kMode8: return launch_mfma<kInt8, 4, kATiled, false>(epi, a, s);
+    default: return launch_mfma<kInt8, 4, kATiled, true>(epi, a, s);
+  }
 }
 
 }  // namespace
@@ -594,12 +649,8 @@ hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& a, hipStrea
     return hipGetLastError();
   }
   const bool i8 = wdtype == H3X_I8;
-  if (gemm_waves() == 4) {
-    if (a.a_tiled) return i8 ? launch_mfma<true, 2, true>(epi, a, s) : launch_mfma<false, 2, true>(epi, a, s);
-    return i8 ? launch_mfma<true, 2, false>(epi, a, s) : launch_mfma<false, 2, false>(epi, a, s);
-  }
-  if (a.a_tiled) return i8 ? launch_mfma<true, 4, true>(epi, a, s) : launch_mfma<false, 4, true>(epi, a, s);
-  return i8 ? launch_mfma<true, 4, false>(epi, a, s) : launch_mfma<false, 4, false>(epi, a, s);
+  if (a.a_tiled) return i8 ? launch_mode<true, true>(epi, a, s) : launch_mode<false, true>(epi, a, s);
+  return i8 ? launch_mode<true, false>(epi, a, s) : launch_mode<false, false>(epi, a, s);
 }
 
 }  // namespace h3x
