@@ -6,7 +6,7 @@ Default run (one GPU):
     SwiGLU inner 24576, 6 x 32 x 32 video + 256 audio + 512 text tokens, bf16 weights and
     activations with float32 accumulation. `value` = algorithmic block FLOPs / time (TFLOP/s).
   * roofline of the dominant kernel (the gate/up + SwiGLU GEMM), timed with HIP events around
-    its launches on the launch stream inside the timed profile pass.
+    its launches on the launch stream inside the timed region.
   * cpu_baseline: the float64 NumPy oracle on a bounded sample of the same block (all K/V rows,
     a few query rows), on this host's cores.
   * denoise: ms per sampler step for the 45-block / 20-step / reuse-2 schedule, the same with
@@ -39,10 +39,14 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-denoise", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=16, help="query rows in the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=64, help="query rows in the oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time")
     p.add_argument("--traffic", type=str, default=None,
-                   help="JSON file with measured HBM bytes per launch of the dominant kernel")
+                   help="counter summary with the dominant kernel's HBM bytes per launch "
+                        "(default: the one under profiles/)")
     p.add_argument("--only-block", action="store_true", help="block timing only (for profilers)")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="also run a 1 GiB device copy (byte-counter calibration)")
     return p.parse_args()
 
 
@@ -56,6 +60,26 @@ def gemm_flops(m, n, k):
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic(path):
+    """HBM bytes per launch of the dominant GEMM from the committed counter summary, or None when
+    the GEMM source has changed since the counters were taken."""
+    import hashlib
+
+    path = path or os.path.join(ROOT, "profiles", "gemm_gate_up_swiglu_block6912_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path, encoding="utf-8"):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "video_diffusion_transformer_02_amd", "csrc", "k_gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def bench_block(args, B, torch, synth):
@@ -78,20 +102,25 @@ def bench_block(args, B, torch, synth):
     for _ in range(args.warmup):
         B.dit_block_forward(cfg, g, pb, modd, x, ws)
     torch.cuda.synchronize()
+    # Timed region: K steps; every launch inside is bracketed by HIP events on its own stream
+    # (the per-kernel durations below), the wall clock gives the step time.
+    B.profile_begin()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         B.dit_block_forward(cfg, g, pb, modd, x, ws)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    prof = B.profile_end()
     flops = block_flops(n, d, f)
     log(f"[bench] block {ms:.3f} ms  {flops / ms / 1e9:.1f} TFLOP/s")
-
-    # Per-kernel event timing over the same number of steps (separate pass).
-    B.profile_begin()
-    for _ in range(args.steps):
-        B.dit_block_forward(cfg, g, pb, modd, x, ws)
-    prof = B.profile_end()
-    torch.cuda.synchronize()
+    if args.copy_calib:
+        # A plain copy of known size, for calibrating hardware byte counters.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            B.copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
     kern = {}
     kflops = {
         "gemm_qkv_rope": gemm_flops(n, 3 * d, d),
@@ -113,10 +142,7 @@ def bench_block(args, B, torch, synth):
     dom = "gemm_gate_up_swiglu"
     dom_ms = kern[dom]["avg_ms"]
     achieved = kflops[dom] / dom_ms / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        t = json.load(open(args.traffic))
-        traffic = t.get(dom)
+    traffic = measured_traffic(args.traffic)
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": dom_ms}
@@ -125,7 +151,8 @@ def bench_block(args, B, torch, synth):
 
 
 def cpu_baseline(args, state):
-    """The oracle on a bounded sample of the block: all rows' K/V, a few query rows."""
+    """The oracle on a bounded sample of the block: K/V of all rows, 64 sampled query rows;
+    repeated until about 10 s of CPU time have passed."""
     import synth
     from oracle import dit
     from oracle.geometry import Geometry
@@ -137,19 +164,24 @@ def cpu_baseline(args, state):
     rows = synth.sample_rows(w)[: args.cpu_rows]
     n, d, f = geom.n_tokens, w.d_model, w.ffn_inner
     r = len(rows)
+    # K and V of all n rows; Q, attention, out-projection and MLP of the r sampled rows.
     flops = 2.0 * 2 * n * d * d + 2.0 * r * d * d + 4.0 * r * n * d + 2.0 * r * d * d + 2.0 * r * d * 3 * f
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count()
-    t0 = time.perf_counter()
-    dit.block_forward(x, vals, state["mod"], geom, w.n_heads, rows=rows)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        dit.block_forward(x, vals, state["mod"], geom, w.n_heads, rows=rows)
+        reps += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
     dt = time.perf_counter() - t0
-    log(f"[bench] oracle sample: {r} query rows, {flops / 1e12:.3f} TFLOP in {dt:.1f} s on {cores} threads")
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"one block at the same shape, {r} of {n} query rows (K/V of all {n} rows), "
-                      f"{flops / 1e12:.3f} TFLOP in {dt:.1f} s"}
+    log(f"[bench] oracle sample: {reps} x ({r} query rows, {flops / 1e12:.3f} TFLOP) in {dt:.1f} s on {cores} threads")
+    return {"value": round(reps * flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"one block at the same shape: K/V of all {n} rows plus {r} of {n} query rows "
+                      f"({flops / 1e12:.3f} TFLOP per pass), {reps} passes in {dt:.1f} s"}
 
 
 def bench_denoise(args, B, torch, synth):
