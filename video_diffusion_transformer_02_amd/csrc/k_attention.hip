@@ -3,13 +3,14 @@
 //
 //  * attn_mfma_kernel (bfloat16, Dh = 128): flash attention with online softmax. A workgroup
 //    of four waves owns 128 queries of one head (32 per wave) and walks the keys in tiles of
-//    64, double-buffered in LDS (K tile [64 x 128], V^T tile [128 x 64], 16-byte chunks
-//    XOR-swizzled by row). Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that
-//    a lane holds 32 scores of a single query: the running max needs one cross-lane exchange
-//    (lane ^ 32) per tile, the running sum none until the end. The probabilities are already
-//    in the B-operand layout of O^T += V^T P^T, so they never leave registers; V^T is read from
-//    LDS in the matching key order. Scores are scaled into base-2 exponent units once
-//    (log2(e) / sqrt(Dh)) and exponentiated with the hardware exp2.
+//    64, double-buffered in LDS and fetched by buffer loads that write LDS directly. Each wave
+//    computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that a lane holds 32 scores of a
+//    single query: the running max needs one cross-lane exchange (lane ^ 32) per tile, the
+//    running sum none until the end. The probabilities are already in the B-operand layout of
+//    O^T += V^T P^T, so they never leave registers. Scores are scaled into base-2 exponent
+//    units inside the exponent's FMA and exponentiated with the hardware exp2; the running max
+//    is lazy (it moves only when a tile exceeds it by 2^8), which removes nearly all rescales
+//    of the output accumulator while keeping every probability below 2^8.
 //  * attn_f32_kernel: float32, one thread per (query, head), online softmax over keys; the
 //    k and v reads of a wave are broadcasts (all its lanes read the same key).
 #include <math.h>
@@ -23,20 +24,26 @@ constexpr int kThreads = 256;
 constexpr int kDh = 128;
 constexpr int kBQ = 128;  // queries per workgroup
 constexpr int kBK = 64;   // keys per tile
-constexpr int kTileK = kBK * kDh * 2;   // bytes of the K tile
-constexpr int kTileV = kDh * kBK * 2;   // bytes of the V^T tile
-constexpr int kStage = kTileK + kTileV;
+constexpr int kTile = kBK * kDh * 2;  // bytes of one K tile or one V^T tile
+constexpr int kVBase = 2 * kTile;     // LDS: K stage 0 | K stage 1 | V^T stage 0 | V^T stage 1
+// The running max only moves when a tile's max exceeds it by more than this many powers of two,
+// so probabilities stay below 2^kLazy; the final normalisation divides the same factor out of
+// the numerator and the denominator.
+constexpr float kLazy = 8.0f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// K tile: [64 keys][128 dims] = 16 chunks of 16 bytes per row, chunk index ^ (row & 15). Rows
-// are 256 bytes (a full bank cycle), so 8 consecutive rows read at one chunk hit 8 distinct
-// 16-byte bank groups.
-__device__ __forceinline__ int k_off(int row, int c) { return row * 256 + ((c ^ (row & 15)) << 4); }
-// V^T tile: [128 dims][64 keys] = 8 chunks per 128-byte row, chunk index ^ ((row >> 1) & 7):
-// the 8-byte reads of 16 consecutive rows (even rows in one half of the banks, odd rows in the
-// other) then fall on 16 distinct bank pairs.
-__device__ __forceinline__ int v_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
+// K tile in LDS: [64 rows][128 dims], 256-byte rows of 16 chunks of 16 bytes, chunk index
+// ^ (row & 15), so the 16 rows read by 16 lanes at one chunk fall on distinct banks. LDS row p
+// holds key sigma(p) of the tile, sigma swapping bits 2 and 3: the S^T accumulator rows then
+// come out in the order in which the P^T operand of O^T += V^T P^T wants its keys, and each
+// lane's V^T operand is 8 consecutive keys, one 16-byte read.
+__device__ __forceinline__ int key_of_row(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+// V^T tile in LDS: [128 dims][64 keys], 128-byte rows of 8 chunks, chunk index ^ f(row) with
+// f(r) = (r ^ (r >> 3 & 1)) & 7: rows 0..7 get distinct f, and so do the even and the odd rows
+// of 0..15, so 16-byte reads of 16 consecutive rows at one chunk are conflict-free whether the
+// LDS serves 128 or 256 bytes per cycle.
+__device__ __forceinline__ int v_swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ k,
@@ -44,7 +51,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
                                                                  uint16_t* __restrict__ o,
                                                                  int n, int n_pad, int n_heads,
                                                                  int qblocks, int o_tiled) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTile];
 
   const int total = n_heads * qblocks;
   const int per_xcd = gridDim.x / 8;
@@ -68,8 +75,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
   }
 
   // K and V^T tiles stream straight into LDS (buffer_load_dwordx4 ... lds: lane l's 16 bytes
-  // land at the wave's 1 KB piece + 16 l); each lane fetches the chunk that the swizzle places
-  // at its LDS position.
+  // land at the wave's 1 KB piece + 16 l); each lane fetches the chunk that the row order and
+  // the swizzle place at its LDS position.
   const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(k), 0, static_cast<int>(static_cast<int64_t>(n_pad) * d * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(
@@ -77,17 +84,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
   uint32_t k_voff[4], v_voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int kr = 4 * (4 * i + wave) + (lane >> 4);          // key row of the K tile
+    const int kr = 4 * (4 * i + wave) + (lane >> 4);          // LDS row of the K tile
     const int kc = (lane & 15) ^ (kr & 15);
-    k_voff[i] = static_cast<uint32_t>((kr * d + head * kDh + kc * 8) * 2);
+    k_voff[i] = static_cast<uint32_t>((key_of_row(kr) * d + head * kDh + kc * 8) * 2);
     const int vr = 8 * (4 * i + wave) + (lane >> 3);          // dim row of the V^T tile
-    const int vc = (lane & 7) ^ ((vr >> 1) & 7);
+    const int vc = (lane & 7) ^ v_swz(vr);
     v_voff[i] = static_cast<uint32_t>(((static_cast<int64_t>(head) * kDh + vr) * n_pad + vc * 8) * 2);
   }
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  auto issue_tile = [&](int kb) {
-    uint8_t* sk = smem + (kb & 1) * kStage;
-    uint8_t* sv = sk + kTileK;
+  auto issue_tile = [&](int kb, int stage) {
+    uint8_t* sk = smem + stage * kTile;
+    uint8_t* sv = smem + kVBase + stage * kTile;
     const uint32_t ko = static_cast<uint32_t>(kb) * kBK * static_cast<uint32_t>(d) * 2;
     const uint32_t vo = static_cast<uint32_t>(kb) * kBK * 2;
 #pragma unroll
@@ -98,6 +105,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (lds_ptr)(sv + (4 * i + wave) * 1024), 16, v_voff[i], vo, 0, 0);
   };
 
+  // Per-lane LDS read offsets, fixed for the whole key loop (stage and block offsets are
+  // immediates): K rows li (+32) at chunk 2s + hi, V^T rows li (+32 db) at chunk 2j + hi.
+  int k_rd[8], v_rd[4];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) k_rd[s] = li * 256 + (((2 * s + hi) ^ (li & 15)) << 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v_rd[j] = li * 128 + (((2 * j + hi) ^ v_swz(li)) << 4);
+
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -105,90 +120,101 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;  // running max in base-2 exponent units, partial sum
   const float c = 1.4426950408889634f / sqrtf(static_cast<float>(kDh));
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   const int ktiles = (n + kBK - 1) / kBK;
-  issue_tile(0);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int full = n / kBK;
 
-  for (int kb = 0; kb < ktiles; ++kb) {
-    if (kb + 1 < ktiles) issue_tile(kb + 1);
-    const uint8_t* sk = smem + (kb & 1) * kStage;
-    const uint8_t* sv = sk + kTileK;
+  auto tile = [&]<int kStage, bool kTail>(int kb) {
+    if (kb + 1 < ktiles) issue_tile(kb + 1, kStage ^ 1);
+    const uint8_t* sk = smem + kStage * kTile;
+    const uint8_t* sv = smem + kVBase + kStage * kTile;
 
-    // S^T for keys kb*64 + 32*kh + (8b + 4hi + r), query qrow.
+    // S^T: sacc[kh] element 4b + r holds key 32kh + 16(b >> 1) + 8hi + 4(b & 1) + r of the tile.
+    const f32x16 zero = {};
     f32x16 sacc[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
+      sacc[kh] = zero;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(sk + k_off(32 * kh + li, 2 * s + hi)));
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(sk + kh * 8192 + k_rd[s]));
         sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kh], 0, 0, 0);
       }
     }
-
-    // Online softmax: the running max is kept in base-2 units; the score scale is folded into
-    // the exponent's fused multiply-add.
-    float mx = -INFINITY;
-    if ((kb + 1) * kBK > n) {
+    if constexpr (kTail) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = kb * kBK + 32 * kh + 8 * (e >> 2) + 4 * hi + (e & 3);
+          const int b = e >> 2;
+          const int key = kb * kBK + 32 * kh + 16 * (b >> 1) + 8 * hi + 4 * (b & 1) + (e & 3);
           if (key >= n) sacc[kh][e] = -INFINITY;
         }
     }
+
+    // Online softmax in base-2 units with the score scale folded into the exponent's FMA.
+    float mx = -INFINITY;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kh][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kh][e], c, -m_new));
-        sacc[kh][e] = pv;
-        psum += pv;
-      }
-    l_run = fmaf(l_run, alpha, psum);
-    if (__ballot(alpha != 1.0f)) {  // the max moved for some query of this wave
+    const float mt = mx * c;
+    if (__ballot(mt > m_run + kLazy)) {  // some query of this wave outgrew its lazy max
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
     }
 
-    // P^T fragments: for 16-key group j, element e is key 16j + 8(e/4) + 4hi + e%4.
+    // P^T fragments: pf[j] element e is key 16j + 8hi + e, built from bfloat16 pairs; the row
+    // sum is taken over the same bfloat16 values that enter the product.
     bf16x8 pf[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      bf16x2 pp[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int b = 2 * (j & 1) + (e >> 2);
-        pf[j][e] = static_cast<__bf16>(sacc[j >> 1][4 * b + (e & 3)]);
+      for (int t = 0; t < 4; ++t) {
+        const int b = 2 * (j & 1) + (t >> 1);
+        const int e0 = 4 * b + 2 * (t & 1);
+        pp[t] = bf16x2{static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[j >> 1][e0], c, -m_run))),
+                       static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[j >> 1][e0 + 1], c, -m_run)))};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, l_run, false);
       }
+      pf[j] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                      __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
 
     // O^T[dim][query] += V^T P^T.
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int row = 32 * db + li;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(sv + v_off(row, 2 * j) + 8 * hi);
-        const u32x2 hi2 = *reinterpret_cast<const u32x2*>(sv + v_off(row, 2 * j + 1) + 8 * hi);
-        const bf16x8 a = as_bf16x8(u32x4{lo.x, lo.y, hi2.x, hi2.y});
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(sv + db * 4096 + v_rd[j]));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[db], 0, 0, 0);
       }
 
     // Tile kb+1 has landed (own loads) and every wave is done with tile kb's stage.
     if (kb + 1 < ktiles) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  issue_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  int kb = 0;
+  for (; kb + 2 <= full; kb += 2) {
+    tile.template operator()<0, false>(kb);
+    tile.template operator()<1, false>(kb + 1);
+  }
+  if (kb < full) {
+    tile.template operator()<0, false>(kb);
+    if (full < ktiles) tile.template operator()<1, true>(kb + 1);
+  } else if (full < ktiles) {
+    tile.template operator()<0, true>(kb);
   }
 
   const float l = l_run + __shfl_xor(l_run, 32, 64);
