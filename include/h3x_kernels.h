@@ -37,9 +37,16 @@ h3x_status h3x_qkv_project(const h3x_block_cfg *cfg, const h3x_geom *geom, const
                            const void *w_qkv, const void *s_qkv, const void *rope_table,
                            void *q, void *k, void *vt, void *stream);
 
-/* o (dev [N x d] act type) = per-head softmax(q k^T / sqrt(Dh)) v over all N keys. */
+/* o (dev [N x d] act type) = per-head softmax(q k^T / sqrt(Dh)) v over all N keys.
+ * bfloat16: the work (128 queries of one head per workgroup) is planned for `slots` workgroups
+ * running at once (0 = two per compute unit of the current device, at most 1024); the queries
+ * of a last, partly filled round are split over key ranges whose partial results go to ws (dev,
+ * h3x_attention_workspace_bytes for the same arguments, 0 when nothing is split) and are merged
+ * by a second kernel. float32 needs no workspace. */
+size_t h3x_attention_workspace_bytes(const h3x_block_cfg *cfg, int64_t n_tokens, int32_t slots);
 h3x_status h3x_attention(const h3x_block_cfg *cfg, int64_t n_tokens, const void *q,
-                         const void *k, const void *vt, void *o, void *stream);
+                         const void *k, const void *vt, void *o, int32_t slots, void *ws,
+                         size_t ws_bytes, void *stream);
 
 /* x (dev [M x d] act type, in place) += gate (dev [d] float32) * (a @ W^T), for kind H3X_W_OUT
  * (a: [M x d]) or H3X_W_DOWN (a: [M x F]); w packed, s its int8 scales or NULL. */

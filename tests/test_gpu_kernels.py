@@ -160,6 +160,34 @@ def test_attention(B, wl, tol, n, sharp):
     assert rel_l2(host(o), ref) < tol
 
 
+@pytest.mark.parametrize("slots", [32, 24, 10, 100, 0])
+def test_attention_work_split(B, record, slots):
+    """The work plan for `slots` resident workgroups, for 1000 tokens and 4 heads (32 items of
+    128 queries, 16 key tiles): 32 runs every item whole; 24 and 10 leave a last round of 8 and
+    2 items cut into 3 and 4 key pieces; 100 and the device's default cut all 32 items (3 pieces
+    of 6 tiles, or one tile each). Every plan agrees with the oracle, and with the plan for one
+    slot (never split) up to the merge's rounding."""
+    wl = SMALL
+    cfg = binding_cfg(wl)
+    n, d = 1000, wl.d_model
+    npad = B.pad_rows(n)
+    rng = np.random.default_rng(7)
+    qv = synth.storage_values(rng.standard_normal((n, d)).astype(np.float32) * np.float32(4.0), "bf16")
+    kv = synth.storage_values(rng.standard_normal((n, d)).astype(np.float32), "bf16")
+    vv = synth.storage_values(rng.standard_normal((n, d)).astype(np.float32), "bf16")
+    qp, kp = np.zeros((npad, d), np.float32), np.zeros((npad, d), np.float32)
+    vtp = np.zeros((d, npad), np.float32)
+    qp[:n], kp[:n], vtp[:, :n] = qv, kv, vv.T
+    args = (to_dev(qp, "bf16"), to_dev(kp, "bf16"), to_dev(vtp, "bf16"))
+    o = host(B.attention(cfg, n, *args, slots=slots))
+    whole = host(B.attention(cfg, n, *args, slots=1))
+    ref = dit.attention(qv, kv, vv, wl.n_heads)
+    err = rel_l2(o, ref)
+    record(f"attention_work_split[slots={slots}]", err, 5e-3)
+    assert err < 5e-3
+    np.testing.assert_allclose(o, whole, rtol=2e-2, atol=2e-2)
+
+
 def test_attention_invariants(B):
     """V == 1 gives O == 1 exactly up to rounding; identical keys give the mean of V."""
     wl = SMALL

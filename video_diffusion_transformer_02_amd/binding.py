@@ -103,7 +103,8 @@ SIGNATURES = {
     "h3x_rope_table_bytes": (_SZ, [_CFG, _GEOM]),
     "h3x_rope_table": (_I32, [_CFG, _GEOM, _P, _P]),
     "h3x_qkv_project": (_I32, [_CFG, _GEOM, _P, _P, _P, _P, _P, _P, _P, _P]),
-    "h3x_attention": (_I32, [_CFG, _I64, _P, _P, _P, _P, _P]),
+    "h3x_attention_workspace_bytes": (_SZ, [_CFG, _I64, _I32]),
+    "h3x_attention": (_I32, [_CFG, _I64, _P, _P, _P, _P, _I32, _P, _SZ, _P]),
     "h3x_linear_residual": (_I32, [_CFG, _I32, _I64, _P, _P, _P, _P, _P, _P]),
     "h3x_linear_swiglu": (_I32, [_CFG, _I64, _P, _P, _P, _P, _P]),
     "h3x_linear_f32out": (_I32, [_CFG, _I32, _I64, _P, _P, _P, _P, _P]),
@@ -290,9 +291,13 @@ def qkv_project(cfg, geom, y, w_qkv, s_qkv=None, table=None):
     return q, k, vt
 
 
-def attention(cfg, n_tokens, q, k, vt, o=None):
+def attention(cfg, n_tokens, q, k, vt, o=None, slots=0):
+    """slots: concurrently resident workgroups the work is planned for (0 = the device's)."""
     o = torch.empty(n_tokens, cfg.d_model, dtype=cfg.act_dtype, device=q.device) if o is None else o
-    _check(lib().h3x_attention(ctypes.byref(cfg), n_tokens, _p(q), _p(k), _p(vt), _p(o), _stream()), "attention")
+    nbytes = lib().h3x_attention_workspace_bytes(ctypes.byref(cfg), n_tokens, slots)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().h3x_attention(ctypes.byref(cfg), n_tokens, _p(q), _p(k), _p(vt), _p(o), slots, _p(ws), nbytes,
+                               _stream()), "attention")
     return o
 
 

@@ -156,8 +156,19 @@ struct BlockWs {
   uint8_t* o;      // [n_pad x d]
   uint8_t* h;      // [n_pad x F], aliases q, k, vt, o (dead once h is produced)
   uint8_t* rope;   // rope table of the geometry
+  uint8_t* attn;   // partial results of key-split attention workgroups
   size_t bytes;
 };
+
+// Upper bound of attention_ws_bytes over every device and bfloat16 attention kernel: at most
+// kAttnMaxPieceQueries queries in pieces, and never more than one 256-query piece per
+// (128-query block, key tile).
+size_t attn_region_bytes(const h3x_block_cfg* c, int64_t n) {
+  if (c->act != H3X_BF16) return 0;
+  const size_t cap = static_cast<size_t>(kAttnMaxPieceQueries / 128) * attn_part_bytes(128);
+  const size_t per_tile = static_cast<size_t>((n + 127) / 128) * c->n_heads * ((n + 63) / 64) * attn_part_bytes(256);
+  return per_tile < cap ? per_tile : cap;
+}
 
 // Activation arenas by lifetime: R2 holds y (norm before attention), then y2 (norm before the
 // MLP); R1 holds q, k, v^T and the attention output o, then the SwiGLU hidden h.
@@ -173,7 +184,8 @@ BlockWs block_layout(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* base) {
   w.y = base + off; off = align256(off + nd);
   w.q = base + off; w.k = w.q + nd; w.vt = w.k + nd; w.o = w.vt + nd; w.h = w.q;
   off = align256(off + r1);
-  w.rope = base + off; off += rope_bytes(c, g);
+  w.rope = base + off; off = align256(off + rope_bytes(c, g));
+  w.attn = base + off; off += attn_region_bytes(c, w.n);
   w.bytes = off;
   return w;
 }
@@ -251,7 +263,8 @@ h3x_status block_forward_impl(const h3x_block_cfg* c, const h3x_geom* g, const h
   qa.q = ws.q; qa.kk = ws.k; qa.vt = ws.vt; qa.geom = gd; qa.rope = rd;
   H3X_LAUNCH(gemm_name(EPI_QKV), s, launch_gemm(c->act, c->weight, EPI_QKV, qa, s));
 
-  H3X_LAUNCH("attention", s, launch_attention(c->act, n, ws.n_pad, c->n_heads, c->head_dim, ws.q, ws.k, ws.vt, ws.o, tiled, s));
+  H3X_LAUNCH("attention", s, launch_attention(c->act, n, ws.n_pad, c->n_heads, c->head_dim, ws.q, ws.k, ws.vt, ws.o, tiled,
+                                              attention_slots(0), ws.attn, s));
 
   GemmArgs oa = gemm_args(c, H3X_W_OUT, n, ws.o, w->out, w->s_out);
   oa.a_tiled = tiled;
@@ -470,10 +483,14 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
     const h3x_geom* gb = merged ? &gm : g;
     bw.n = geom_tokens(gb);
     bw.n_pad = round_up(bw.n, 256);
-    // Re-derive the arena pointers for the (smaller) merged sequence inside the same memory.
+    // Re-derive the y and R1 arenas for the (smaller) merged sequence inside the unmerged ones.
+    // Only those two are re-laid: past them lies the unmerged rope table, which the blocks after
+    // the reduced range still read, so the merged rope table and the attention pieces keep
+    // regions of their own (the unmerged attention region bounds the merged one).
     if (merged) {
       BlockWs m = block_layout(c, gb, lay.blk.y);
       m.rope = lay.rope_m;
+      m.attn = lay.blk.attn;
       bw = m;
     }
     if ((st = block_forward_impl(c, gb, &st_->blocks[b], st_->mod + b * mod_stride,
@@ -531,15 +548,26 @@ h3x_status h3x_qkv_project(const h3x_block_cfg* c, const h3x_geom* g, const void
   return H3X_OK;
 }
 
+size_t h3x_attention_workspace_bytes(const h3x_block_cfg* c, int64_t n_tokens, int32_t slots) {
+  if (check_cfg(c) != H3X_OK || n_tokens < 1 || n_tokens > (int64_t(1) << 26) || slots < 0) return 0;
+  return attention_ws_bytes(c->act, n_tokens, c->n_heads, attention_slots(slots));
+}
+
 h3x_status h3x_attention(const h3x_block_cfg* c, int64_t n_tokens, const void* q, const void* k,
-                         const void* vt, void* o, void* stream) {
+                         const void* vt, void* o, int32_t slots, void* ws, size_t ws_bytes, void* stream) {
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
   if (n_tokens < 1 || n_tokens > (int64_t(1) << 26)) return fail(H3X_EINVAL, "attention: bad n_tokens");
+  if (slots < 0) return fail(H3X_EINVAL, "attention: negative slots");
   if (!q || !k || !vt || !o || !aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
     return fail(H3X_EINVAL, "attention: NULL or misaligned pointer");
+  const int sl = attention_slots(slots);
+  const size_t need = attention_ws_bytes(c->act, n_tokens, c->n_heads, sl);
+  if (need > 0 && (!ws || !aligned16(ws))) return fail(H3X_EINVAL, "attention: NULL or misaligned workspace");
+  if (ws_bytes < need) return fail(H3X_EWORKSPACE, "attention: workspace too small");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  H3X_LAUNCH("attention", s, launch_attention(c->act, n_tokens, round_up(n_tokens, 256), c->n_heads, c->head_dim, q, k, vt, o, 0, s));
+  H3X_LAUNCH("attention", s, launch_attention(c->act, n_tokens, round_up(n_tokens, 256), c->n_heads, c->head_dim, q, k, vt, o, 0,
+                                              sl, ws, s));
   return H3X_OK;
 }
 

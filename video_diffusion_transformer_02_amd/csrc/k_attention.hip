@@ -11,6 +11,8 @@
 //    units inside the exponent's FMA and exponentiated with the hardware exp2; the running max
 //    is lazy (it moves only when a tile exceeds it by 2^8), which removes nearly all rescales
 //    of the output accumulator while keeping every probability below 2^8.
+//    The queries of a last, partly filled round of workgroups are split over key ranges; the
+//    pieces' partial results (unnormalised O, lazy max, sum) are merged by attn_combine_kernel.
 //  * attn_f32_kernel: float32, one thread per (query, head), online softmax over keys; the
 //    k and v reads of a wave are broadcasts (all its lanes read the same key).
 #include <math.h>
@@ -50,15 +52,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
                                                                  const uint16_t* __restrict__ vt,
                                                                  uint16_t* __restrict__ o,
                                                                  int n, int n_pad, int n_heads,
-                                                                 int qblocks, int o_tiled) {
+                                                                 AttnPlan plan, int full_grid,
+                                                                 int o_tiled, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTile];
 
-  const int total = n_heads * qblocks;
-  const int per_xcd = gridDim.x / 8;
-  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (logical >= total) return;
-  const int head = logical / qblocks;
-  const int qb = logical % qblocks;
+  // Whole items first (blocks 0 .. full_grid-1, each XCD a contiguous run of items so that the
+  // workgroups of one head share its K/V tiles in that XCD's L2), then the key pieces of the
+  // last round's items (tiles t0 .. t1-1 of one item each).
+  int item, t0, t1, slot = -1;
+  if (static_cast<int>(blockIdx.x) < full_grid) {
+    const int per_xcd = full_grid / 8;
+    const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (logical >= plan.full_items) return;
+    item = logical;
+    t0 = 0;
+    t1 = plan.ktiles;
+  } else {
+    slot = blockIdx.x - full_grid;
+    item = plan.full_items + slot / plan.pieces;
+    t0 = (slot % plan.pieces) * plan.tiles;
+    t1 = min(plan.ktiles, t0 + plan.tiles);
+  }
+  const int head = item / plan.qblocks;
+  const int qb = item % plan.qblocks;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -122,11 +138,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
   const float c = 1.4426950408889634f / sqrtf(static_cast<float>(kDh));
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  const int ktiles = (n + kBK - 1) / kBK;
-  const int full = n / kBK;
 
   auto tile = [&]<int kStage, bool kTail>(int kb) {
-    if (kb + 1 < ktiles) issue_tile(kb + 1, kStage ^ 1);
+    if (kb + 1 < t1) issue_tile(kb + 1, kStage ^ 1);
     const uint8_t* sk = smem + kStage * kTile;
     const uint8_t* sv = smem + kVBase + kStage * kTile;
 
@@ -200,24 +214,43 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
       }
 
     // Tile kb+1 has landed (own loads) and every wave is done with tile kb's stage.
-    if (kb + 1 < ktiles) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kb + 1 < t1) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  issue_tile(0, 0);
+  // Tiles t0 .. t1-1; only the sequence's last tile can be ragged.
+  const int tail = (t1 == plan.ktiles && n % kBK != 0) ? 1 : 0;
+  const int nfull = t1 - t0 - tail;
+  issue_tile(t0, 0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  int kb = 0;
-  for (; kb + 2 <= full; kb += 2) {
-    tile.template operator()<0, false>(kb);
-    tile.template operator()<1, false>(kb + 1);
+  int i = 0;
+  for (; i + 2 <= nfull; i += 2) {
+    tile.template operator()<0, false>(t0 + i);
+    tile.template operator()<1, false>(t0 + i + 1);
   }
-  if (kb < full) {
-    tile.template operator()<0, false>(kb);
-    if (full < ktiles) tile.template operator()<1, true>(kb + 1);
-  } else if (full < ktiles) {
-    tile.template operator()<0, true>(kb);
+  if (i < nfull) {
+    tile.template operator()<0, false>(t0 + i);
+    if (tail) tile.template operator()<1, true>(t0 + i + 1);
+  } else if (tail) {
+    tile.template operator()<0, true>(t0 + i);
   }
 
   const float l = l_run + __shfl_xor(l_run, 32, 64);
+  if (slot >= 0) {
+    // Partial result of a key piece: unnormalised O (fp32, [query][dim]), lazy max, row sum.
+    float* rec = part + static_cast<size_t>(slot) * (attn_part_bytes(kBQ) / 4);
+    const int ql = wave * 32 + li;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        *reinterpret_cast<f32x4*>(rec + ql * kDh + 32 * db + 8 * b + 4 * hi) =
+            f32x4{oacc[db][4 * b + 0], oacc[db][4 * b + 1], oacc[db][4 * b + 2], oacc[db][4 * b + 3]};
+    if (hi == 0) {
+      rec[kBQ * kDh + ql] = m_run;
+      rec[kBQ * kDh + kBQ + ql] = l;
+    }
+    return;
+  }
   const float inv = 1.0f / l;
   if (qrow < n) {
     uint16_t* op = o + qrow * d + head * kDh;
@@ -236,6 +269,49 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
           *reinterpret_cast<u32x2*>(op + dim) = u32x2{w0, w1};
       }
   }
+}
+
+// Merges the key pieces of the last round's items: with M the largest piece max, O = sum_p O_p
+// 2^(m_p - M) divided by sum_p l_p 2^(m_p - M). One thread per (query, 8 dims); a workgroup
+// covers 16 queries of one item.
+__global__ __launch_bounds__(256) void attn_combine_kernel(uint16_t* __restrict__ o,
+                                                           const float* __restrict__ part, int n,
+                                                           int n_heads, AttnPlan plan, int o_tiled) {
+  constexpr size_t kRec = attn_part_bytes(kBQ) / 4;
+  const int r = blockIdx.x / (kBQ / 16);
+  const int item = plan.full_items + r;
+  const int head = item / plan.qblocks, qb = item % plan.qblocks;
+  const int ql = (blockIdx.x % (kBQ / 16)) * 16 + (threadIdx.x >> 4);
+  const int dim = 8 * (threadIdx.x & 15);
+  const int64_t qrow = static_cast<int64_t>(qb) * kBQ + ql;
+  if (qrow >= n) return;
+  const int64_t d = static_cast<int64_t>(n_heads) * kDh;
+  const float* rec0 = part + static_cast<size_t>(r) * plan.pieces * kRec;
+  float mmax = -INFINITY;
+  for (int p = 0; p < plan.pieces; ++p) mmax = fmaxf(mmax, rec0[p * kRec + kBQ * kDh + ql]);
+  float lsum = 0.f;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < plan.pieces; ++p) {
+    const float* rec = rec0 + p * kRec;
+    const float w = __builtin_amdgcn_exp2f(rec[kBQ * kDh + ql] - mmax);
+    lsum = fmaf(rec[kBQ * kDh + kBQ + ql], w, lsum);
+    a0 += *reinterpret_cast<const f32x4*>(rec + ql * kDh + dim) * w;
+    a1 += *reinterpret_cast<const f32x4*>(rec + ql * kDh + dim + 4) * w;
+  }
+  const float inv = 1.0f / lsum;
+  u32x4 packed;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    packed[t] = static_cast<uint32_t>(f32_to_bf16_bits(a0[2 * t] * inv)) |
+                (static_cast<uint32_t>(f32_to_bf16_bits(a0[2 * t + 1] * inv)) << 16);
+    packed[2 + t] = static_cast<uint32_t>(f32_to_bf16_bits(a1[2 * t] * inv)) |
+                    (static_cast<uint32_t>(f32_to_bf16_bits(a1[2 * t + 1] * inv)) << 16);
+  }
+  const int64_t col = static_cast<int64_t>(head) * kDh + dim;
+  if (o_tiled)  // 8 dims = one 16-byte chunk of a slab row
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(o) + slab_offset(qrow, col, d)) = packed;
+  else
+    *reinterpret_cast<u32x4*>(o + qrow * d + col) = packed;
 }
 
 template <int DH>
@@ -278,19 +354,71 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
+int attention_slots(int requested) {
+  constexpr int cap = kAttnMaxPieceQueries / kBQ;
+  if (requested > 0) return requested < cap ? requested : cap;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  // Two workgroups per CU (64 KB of LDS and 2 waves per SIMD each).
+  return 2 * cached[dev] < cap ? 2 * cached[dev] : cap;
+}
+
+AttnPlan attention_plan(int64_t n_tokens, int n_heads, int slots) {
+  AttnPlan p;
+  const int n = static_cast<int>(n_tokens);
+  p.bq = kBQ;
+  p.qblocks = (n + kBQ - 1) / kBQ;
+  p.items = p.qblocks * n_heads;
+  p.ktiles = (n + kBK - 1) / kBK;
+  p.full_items = p.items;
+  p.rem = 0;
+  p.pieces = 1;
+  p.tiles = p.ktiles;
+  const int rounds = p.items / slots, rem = p.items - rounds * slots;
+  int pieces = rem > 0 ? slots / rem : 1;
+  if (pieces > p.ktiles) pieces = p.ktiles;
+  if (pieces >= 2) {
+    p.tiles = (p.ktiles + pieces - 1) / pieces;
+    p.pieces = (p.ktiles + p.tiles - 1) / p.tiles;
+    p.rem = rem;
+    p.full_items = rounds * slots;
+  }
+  return p;
+}
+
+size_t attention_ws_bytes(int act, int64_t n_tokens, int n_heads, int slots) {
+  if (act != H3X_BF16 || n_tokens < 1) return 0;
+  const AttnPlan p = attention_plan(n_tokens, n_heads, slots);
+  return static_cast<size_t>(p.rem) * p.pieces * attn_part_bytes(p.bq);
+}
+
 hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_heads, int head_dim,
                             const void* q, const void* k, const void* vt, void* o, int o_tiled,
-                            hipStream_t s) {
+                            int slots, void* ws, hipStream_t s) {
   if (n_tokens == 0) return hipSuccess;
   const int n = static_cast<int>(n_tokens), np = static_cast<int>(n_pad);
   if (act == H3X_BF16) {
-    const int qblocks = (n + kBQ - 1) / kBQ;
-    const int total = qblocks * n_heads;
-    const int grid = (total + 7) / 8 * 8;
+    const AttnPlan plan = attention_plan(n_tokens, n_heads, slots);
+    const int full_grid = (plan.full_items + 7) / 8 * 8;
+    const int grid = full_grid + plan.rem * plan.pieces;
     attn_mfma_kernel<<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(q),
                                                static_cast<const uint16_t*>(k),
                                                static_cast<const uint16_t*>(vt),
-                                               static_cast<uint16_t*>(o), n, np, n_heads, qblocks, o_tiled);
+                                               static_cast<uint16_t*>(o), n, np, n_heads, plan,
+                                               full_grid, o_tiled, static_cast<float*>(ws));
+    if (plan.rem > 0) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      attn_combine_kernel<<<plan.rem * (kBQ / 16), 256, 0, s>>>(static_cast<uint16_t*>(o),
+                                                                static_cast<const float*>(ws), n,
+                                                                n_heads, plan, o_tiled);
+    }
   } else {
     dim3 grid(static_cast<unsigned>((n + 63) / 64), static_cast<unsigned>(n_heads));
     if (head_dim == 64)

@@ -82,8 +82,22 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& args, hipStream_t s);
+// Work split of the bfloat16 attention over `slots` concurrently resident workgroups. An item
+// is bq queries of one head; items 0 .. full_items-1 run whole, in full rounds of `slots`; the
+// rem items left for a last, partly empty round are cut into `pieces` key ranges of `tiles`
+// 64-key tiles each, whose partial results a second kernel merges.
+struct AttnPlan {
+  int bq, qblocks, items, ktiles;
+  int full_items, rem, pieces, tiles;
+};
+// Partial results of at most 2^17 queries (pieces x bq) are kept: O (fp32, 128 dims), max, sum.
+constexpr int kAttnMaxPieceQueries = 1 << 17;
+constexpr size_t attn_part_bytes(int bq) { return static_cast<size_t>(bq) * (128 * 4 + 2 * 4); }
+int attention_slots(int requested);  // 0 = what the current device runs at once
+AttnPlan attention_plan(int64_t n_tokens, int n_heads, int slots);
+size_t attention_ws_bytes(int act, int64_t n_tokens, int n_heads, int slots);
 hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_heads, int head_dim,
                             const void* q, const void* k, const void* vt, void* o, int o_tiled,
-                            hipStream_t s);
+                            int slots, void* ws, hipStream_t s);
 
 }  // namespace h3x
