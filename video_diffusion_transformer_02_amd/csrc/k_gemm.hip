@@ -1,14 +1,15 @@
 // Projection GEMMs of the block: C = A * W^T with fused epilogues.
 //
 //  * gemm_mfma_kernel: bfloat16 activations, bfloat16 or int8 weights, float32 accumulation on
-//    the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16). 256 x 256 output tile per workgroup,
-//    K step 64, four waves in a 2 x 2 grid each owning 128 x 128 (4 x 4 MFMA blocks of 32 x 32).
-//    Operand tiles are staged through LDS (two stages, 16-byte chunks XOR-swizzled by row so
-//    that the MFMA operand reads are bank-conflict free); the next K step is fetched into
-//    registers while the current one is multiplied. int8 weights are widened to bfloat16 in
-//    registers (exact: |q| <= 127) and their per-row scale is applied in the epilogue.
-//    Workgroups are remapped so that each XCD (own L2) walks a contiguous run of a grouped
-//    tile order: consecutive tiles share weight panels and activation panels.
+//    the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16). 256 x 256 output tile per workgroup of
+//    eight waves (2 x 4, each 128 x 64), K step 32 in a five-stage LDS pipeline filled by
+//    buffer loads that write LDS directly (operands stored as 256 x 32 slabs in LDS order, so a
+//    K step is one contiguous copy). By default the two halves of the workgroup (one wave of
+//    each per SIMD) run ping-pong: while one issues its MFMAs the other reads its next
+//    fragments and streams the next K step, offset by one barrier interval. int8 weights are
+//    widened to bfloat16 in registers (exact: |q| <= 127) and their per-row scale is applied in
+//    the epilogue. Workgroups are remapped so that each XCD (own L2) walks a contiguous run of
+//    a grouped tile order: consecutive tiles share weight panels and activation panels.
 //  * gemm_f32_kernel: float32 activations and weights (small configurations): 64 x 64 tiles,
 //    plain FMA, same epilogues.
 //
@@ -101,8 +102,7 @@ __device__ __forceinline__ void pipeline_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Waves of a workgroup: 2 along M, kWN along N. kWN = 2: four waves, each a 128 x 128 sub-tile
-// (256 accumulator registers, one wave per SIMD). kWN = 4: eight waves, each 128 x 64 (128
+// Waves of a workgroup: 2 along M, kWN along N. kWN = 4: eight waves, each 128 x 64 (128
 // accumulator registers, two waves per SIMD, so one wave's MFMAs can run while the other waits).
 template <int kWN>
 struct Layout {
@@ -610,26 +610,20 @@ hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Schedule of the MFMA GEMM: 4 waves (one 128 x 128 sub-tile each), 8 waves (128 x 64 each,
-// both halves in step), or 8 waves in ping-pong (the default).
-enum GemmMode { kMode4 = 0, kMode8 = 1, kModePP = 2 };
-int gemm_mode() {
+// Schedule of the MFMA GEMM: eight waves (128 x 64 each) in ping-pong (the default), or in step
+// (H3X_GEMM_MODE=w8).
+int gemm_mode_pp() {
   static const int m = [] {
     const char* e = getenv("H3X_GEMM_MODE");
-    if (e && strcmp(e, "w4") == 0) return static_cast<int>(kMode4);
-    if (e && strcmp(e, "w8") == 0) return static_cast<int>(kMode8);
-    return static_cast<int>(kModePP);
+    return (e && strcmp(e, "w8") == 0) ? 0 : 1;
   }();
   return m;
 }
 
 template <bool kInt8, bool kATiled>
 hipError_t launch_mode(int epi, const GemmArgs& a, hipStream_t s) {
-  switch (gemm_mode()) {
-    case kMode4: return launch_mfma<kInt8, 2, kATiled, false>(epi, a, s);
-    case kMode8: return launch_mfma<kInt8, 4, kATiled, false>(epi, a, s);
-    default: return launch_mfma<kInt8, 4, kATiled, true>(epi, a, s);
-  }
+  if (gemm_mode_pp()) return launch_mfma<kInt8, 4, kATiled, true>(epi, a, s);
+  return launch_mfma<kInt8, 4, kATiled, false>(epi, a, s);
 }
 
 }  // namespace
