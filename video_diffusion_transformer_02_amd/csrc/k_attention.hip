@@ -5,12 +5,13 @@
 //    of four waves owns 128 queries of one head (32 per wave) and walks the keys in tiles of
 //    64, double-buffered in LDS and fetched by buffer loads that write LDS directly. Each wave
 //    computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that a lane holds 32 scores of a
-//    single query: the running max needs one cross-lane exchange (lane ^ 32) per tile, the
-//    running sum none until the end. The probabilities are already in the B-operand layout of
-//    O^T += V^T P^T, so they never leave registers. Scores are scaled into base-2 exponent
-//    units inside the exponent's FMA and exponentiated with the hardware exp2; the running max
-//    is lazy (it moves only when a tile exceeds it by 2^8), which removes nearly all rescales
-//    of the output accumulator while keeping every probability below 2^8.
+//    single query: a max needs one cross-lane exchange (lane ^ 32), the running sum none until
+//    the end. The probabilities are already in the B-operand layout of O^T += V^T P^T, so they
+//    never leave registers. Scores are scaled into base-2 exponent units inside the exponent's
+//    FMA and exponentiated with the hardware exp2. The running max is lazy: each tile's
+//    probabilities are first taken against the max as it stands, and only when a query's tile
+//    sum would exceed 2^16 (or is not finite: the first tile) is the tile max formed and the
+//    tile redone, so nearly every tile skips both the max reduction and the O rescale.
 //    The queries of a last, partly filled round of workgroups are split over key ranges; the
 //    pieces' partial results (unnormalised O, lazy max, sum) are merged by attn_combine_kernel.
 //  * attn_f32_kernel: float32, one thread per (query, head), online softmax over keys; the
@@ -28,10 +29,10 @@ constexpr int kBQ = 128;  // queries per workgroup
 constexpr int kBK = 64;   // keys per tile
 constexpr int kTile = kBK * kDh * 2;  // bytes of one K tile or one V^T tile
 constexpr int kVBase = 2 * kTile;     // LDS: K stage 0 | K stage 1 | V^T stage 0 | V^T stage 1
-// The running max only moves when a tile's max exceeds it by more than this many powers of two,
-// so probabilities stay below 2^kLazy; the final normalisation divides the same factor out of
-// the numerator and the denominator.
-constexpr float kLazy = 8.0f;
+// The running max only moves when some query's tile sum of probabilities, taken against the
+// max as it stands, exceeds kSpecMax (so every probability stays <= 2^16); the final
+// normalisation divides the same factor out of the numerator and the denominator.
+constexpr float kSpecMax = 65536.0f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -167,16 +168,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
         }
     }
 
-    // Online softmax in base-2 units with the score scale folded into the exponent's FMA.
-    float mx = -INFINITY;
+    // Online softmax in base-2 units with the score scale folded into the exponent's FMA. The
+    // probabilities are first taken against the running max as it stands; only when some
+    // query's tile sum leaves (0, 2^16] (the first tile, where the max is -inf, or scores that
+    // outgrew the max) is the tile max formed, O and the sum rescaled and the tile redone.
+    bf16x8 pf[4];
+    auto probs = [&](float& lt) {
+      // pf[j] element e is key 16j + 8hi + e, built from bfloat16 pairs; the sum is taken over
+      // the same bfloat16 values that enter the product.
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+      for (int j = 0; j < 4; ++j) {
+        bf16x2 pp[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kh][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mt = mx * c;
-    if (__ballot(mt > m_run + kLazy)) {  // some query of this wave outgrew its lazy max
-      const float m_new = fmaxf(m_run, mt);
+        for (int t = 0; t < 4; ++t) {
+          const int b = 2 * (j & 1) + (t >> 1);
+          const int e0 = 4 * b + 2 * (t & 1);
+          pp[t] = bf16x2{static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[j >> 1][e0], c, -m_run))),
+                         static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[j >> 1][e0 + 1], c, -m_run)))};
+          lt = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, lt, false);
+        }
+        pf[j] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                        __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    float lt = 0.f;
+    probs(lt);
+    if (__ballot(!(lt <= kSpecMax))) {  // also true for inf and NaN sums
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kh][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx * c);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -184,25 +208,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+      lt = 0.f;
+      probs(lt);
     }
-
-    // P^T fragments: pf[j] element e is key 16j + 8hi + e, built from bfloat16 pairs; the row
-    // sum is taken over the same bfloat16 values that enter the product.
-    bf16x8 pf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x2 pp[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int b = 2 * (j & 1) + (t >> 1);
-        const int e0 = 4 * b + 2 * (t & 1);
-        pp[t] = bf16x2{static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[j >> 1][e0], c, -m_run))),
-                       static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[j >> 1][e0 + 1], c, -m_run)))};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, l_run, false);
-      }
-      pf[j] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                      __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+    l_run += lt;
 
     // O^T[dim][query] += V^T P^T.
 #pragma unroll
