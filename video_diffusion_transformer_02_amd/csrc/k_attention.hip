@@ -1,9 +1,11 @@
 // Full bidirectional attention over the joint token sequence, softmax(q k^T / sqrt(Dh)) v per
 // head, with no mask (every token attends to every token).
 //
-//  * attn_mfma_kernel (bfloat16, Dh = 128): flash attention with online softmax. A workgroup
-//    of four waves owns 128 queries of one head (32 per wave) and walks the keys in tiles of
-//    64, double-buffered in LDS and fetched by buffer loads that write LDS directly. Each wave
+//  * attn_mfma8_kernel / attn_mfma_kernel (bfloat16, Dh = 128): flash attention with online
+//    softmax. A workgroup of eight (default) or four waves owns 256 or 128 queries of one head
+//    (32 per wave) and walks the keys in tiles of 64, double-buffered in LDS and fetched by
+//    buffer loads that write LDS directly; the eight-wave form shares each tile between twice
+//    the queries, halving the tile traffic into LDS and through L2. Each wave
 //    computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that a lane holds 32 scores of a
 //    single query: a max needs one cross-lane exchange (lane ^ 32), the running sum none until
 //    the end. The probabilities are already in the B-operand layout of O^T += V^T P^T, so they
@@ -17,15 +19,15 @@
 //  * attn_f32_kernel: float32, one thread per (query, head), online softmax over keys; the
 //    k and v reads of a wave are broadcasts (all its lanes read the same key).
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "launch.h"
 
 namespace h3x {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kDh = 128;
-constexpr int kBQ = 128;  // queries per workgroup
 constexpr int kBK = 64;   // keys per tile
 constexpr int kTile = kBK * kDh * 2;  // bytes of one K tile or one V^T tile
 constexpr int kVBase = 2 * kTile;     // LDS: K stage 0 | K stage 1 | V^T stage 0 | V^T stage 1
@@ -48,13 +50,15 @@ __device__ __forceinline__ int key_of_row(int p) { return (p & ~12) | ((p & 4) <
 // LDS serves 128 or 256 bytes per cycle.
 __device__ __forceinline__ int v_swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
-                                                                 const uint16_t* __restrict__ k,
-                                                                 const uint16_t* __restrict__ vt,
-                                                                 uint16_t* __restrict__ o,
-                                                                 int n, int n_pad, int n_heads,
-                                                                 AttnPlan plan, int full_grid,
-                                                                 int o_tiled, float* __restrict__ part) {
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <int kWaves>
+__device__ __forceinline__ void attn_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                          const uint16_t* __restrict__ vt, uint16_t* __restrict__ o,
+                                          int n, int n_pad, int n_heads, AttnPlan plan, int full_grid,
+                                          int o_tiled, float* __restrict__ part) {
+  constexpr int kBQ = 32 * kWaves;       // queries per workgroup
+  constexpr int kPieces = 16 / kWaves;   // 1 KB pieces of each tile per wave
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTile];
 
   // Whole items first (blocks 0 .. full_grid-1, each XCD a contiguous run of items so that the
@@ -98,28 +102,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
       const_cast<uint16_t*>(k), 0, static_cast<int>(static_cast<int64_t>(n_pad) * d * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(vt), 0, static_cast<int>(static_cast<int64_t>(n_pad) * d * 2), 0x00020000);
-  uint32_t k_voff[4], v_voff[4];
+  uint32_t k_voff[kPieces], v_voff[kPieces];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kr = 4 * (4 * i + wave) + (lane >> 4);          // LDS row of the K tile
+  for (int i = 0; i < kPieces; ++i) {
+    const int kr = 4 * (kWaves * i + wave) + (lane >> 4);     // LDS row of the K tile
     const int kc = (lane & 15) ^ (kr & 15);
     k_voff[i] = static_cast<uint32_t>((key_of_row(kr) * d + head * kDh + kc * 8) * 2);
-    const int vr = 8 * (4 * i + wave) + (lane >> 3);          // dim row of the V^T tile
+    const int vr = 8 * (kWaves * i + wave) + (lane >> 3);     // dim row of the V^T tile
     const int vc = (lane & 7) ^ v_swz(vr);
     v_voff[i] = static_cast<uint32_t>(((static_cast<int64_t>(head) * kDh + vr) * n_pad + vc * 8) * 2);
   }
-  typedef __attribute__((address_space(3))) void* lds_ptr;
   auto issue_tile = [&](int kb, int stage) {
     uint8_t* sk = smem + stage * kTile;
     uint8_t* sv = smem + kVBase + stage * kTile;
     const uint32_t ko = static_cast<uint32_t>(kb) * kBK * static_cast<uint32_t>(d) * 2;
     const uint32_t vo = static_cast<uint32_t>(kb) * kBK * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_k, (lds_ptr)(sk + (4 * i + wave) * 1024), 16, k_voff[i], ko, 0, 0);
+    for (int i = 0; i < kPieces; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_k, (lds_ptr)(sk + (kWaves * i + wave) * 1024), 16, k_voff[i], ko, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (lds_ptr)(sv + (4 * i + wave) * 1024), 16, v_voff[i], vo, 0, 0);
+    for (int i = 0; i < kPieces; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_v, (lds_ptr)(sv + (kWaves * i + wave) * 1024), 16, v_voff[i], vo, 0, 0);
   };
 
   // Per-lane LDS read offsets, fixed for the whole key loop (stage and block offsets are
@@ -280,9 +283,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(const uint16_t* 
   }
 }
 
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ vt,
+                                                           uint16_t* __restrict__ o, int n, int n_pad,
+                                                           int n_heads, AttnPlan plan, int full_grid,
+                                                           int o_tiled, float* __restrict__ part) {
+  attn_body<4>(q, k, vt, o, n, n_pad, n_heads, plan, full_grid, o_tiled, part);
+}
+__global__ __launch_bounds__(512, 1) void attn_mfma8_kernel(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ vt,
+                                                            uint16_t* __restrict__ o, int n, int n_pad,
+                                                            int n_heads, AttnPlan plan, int full_grid,
+                                                            int o_tiled, float* __restrict__ part) {
+  attn_body<8>(q, k, vt, o, n, n_pad, n_heads, plan, full_grid, o_tiled, part);
+}
+
 // Merges the key pieces of the last round's items: with M the largest piece max, O = sum_p O_p
 // 2^(m_p - M) divided by sum_p l_p 2^(m_p - M). One thread per (query, 8 dims); a workgroup
 // covers 16 queries of one item.
+template <int kBQ>
 __global__ __launch_bounds__(256) void attn_combine_kernel(uint16_t* __restrict__ o,
                                                            const float* __restrict__ part, int n,
                                                            int n_heads, AttnPlan plan, int o_tiled) {
@@ -361,10 +382,21 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   }
 }
 
+// Workgroup size of the bfloat16 kernel: eight waves (256 queries sharing each K/V tile, one
+// workgroup per CU; the default), or four (128 queries, two workgroups per CU) with
+// H3X_ATTN_MODE=w4.
+int attn_waves() {
+  static const int w = [] {
+    const char* e = getenv("H3X_ATTN_MODE");
+    return (e && strcmp(e, "w4") == 0) ? 4 : 8;
+  }();
+  return w;
+}
+
 }  // namespace
 
 int attention_slots(int requested) {
-  constexpr int cap = kAttnMaxPieceQueries / kBQ;
+  const int cap = kAttnMaxPieceQueries / (32 * attn_waves());
   if (requested > 0) return requested < cap ? requested : cap;
   static int cached[64] = {0};
   int dev = 0;
@@ -374,15 +406,16 @@ int attention_slots(int requested) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     cached[dev] = cus;
   }
-  // Two workgroups per CU (64 KB of LDS and 2 waves per SIMD each).
-  return 2 * cached[dev] < cap ? 2 * cached[dev] : cap;
+  // Two waves per SIMD: two four-wave workgroups or one eight-wave workgroup per CU.
+  const int per_cu = 8 / attn_waves();
+  return per_cu * cached[dev] < cap ? per_cu * cached[dev] : cap;
 }
 
 AttnPlan attention_plan(int64_t n_tokens, int n_heads, int slots) {
   AttnPlan p;
   const int n = static_cast<int>(n_tokens);
-  p.bq = kBQ;
-  p.qblocks = (n + kBQ - 1) / kBQ;
+  p.bq = 32 * attn_waves();
+  p.qblocks = (n + p.bq - 1) / p.bq;
   p.items = p.qblocks * n_heads;
   p.ktiles = (n + kBK - 1) / kBK;
   p.full_items = p.items;
@@ -416,17 +449,21 @@ hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_head
     const AttnPlan plan = attention_plan(n_tokens, n_heads, slots);
     const int full_grid = (plan.full_items + 7) / 8 * 8;
     const int grid = full_grid + plan.rem * plan.pieces;
-    attn_mfma_kernel<<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(q),
-                                               static_cast<const uint16_t*>(k),
-                                               static_cast<const uint16_t*>(vt),
-                                               static_cast<uint16_t*>(o), n, np, n_heads, plan,
-                                               full_grid, o_tiled, static_cast<float*>(ws));
+    const uint16_t *qq = static_cast<const uint16_t*>(q), *kk = static_cast<const uint16_t*>(k);
+    const uint16_t* vv = static_cast<const uint16_t*>(vt);
+    uint16_t* oo = static_cast<uint16_t*>(o);
+    float* pp = static_cast<float*>(ws);
+    if (plan.bq == 256)
+      attn_mfma8_kernel<<<grid, 512, 0, s>>>(qq, kk, vv, oo, n, np, n_heads, plan, full_grid, o_tiled, pp);
+    else
+      attn_mfma_kernel<<<grid, 256, 0, s>>>(qq, kk, vv, oo, n, np, n_heads, plan, full_grid, o_tiled, pp);
     if (plan.rem > 0) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      attn_combine_kernel<<<plan.rem * (kBQ / 16), 256, 0, s>>>(static_cast<uint16_t*>(o),
-                                                                static_cast<const float*>(ws), n,
-                                                                n_heads, plan, o_tiled);
+      if (plan.bq == 256)
+        attn_combine_kernel<256><<<plan.rem * 16, 256, 0, s>>>(oo, pp, n, n_heads, plan, o_tiled);
+      else
+        attn_combine_kernel<128><<<plan.rem * 8, 256, 0, s>>>(oo, pp, n, n_heads, plan, o_tiled);
     }
   } else {
     dim3 grid(static_cast<unsigned>((n + 63) / 64), static_cast<unsigned>(n_heads));
