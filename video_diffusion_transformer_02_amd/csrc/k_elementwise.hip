@@ -95,6 +95,76 @@ __global__ __launch_bounds__(kThreads) void norm_mod_kernel(const typename E::T*
   }
 }
 
+// kRows rows per workgroup with the rows held in registers (each row read once) and shift /
+// scale loaded once for all kRows rows; kChunks 16-byte chunks per thread and row cover
+// d <= kChunks * 256 * V. Same arithmetic, in the same order, as norm_mod_kernel.
+template <class E, int kChunks, int kRows>
+__global__ __launch_bounds__(kThreads) void norm_rows_kernel(const typename E::T* __restrict__ x,
+                                                             const float* __restrict__ shift,
+                                                             const float* __restrict__ scale,
+                                                             typename E::T* __restrict__ y,
+                                                             int64_t n_rows, int d, float eps,
+                                                             int out_tiled) {
+  constexpr int V = Vec<E>::n;
+  __shared__ float part[kRows][kThreads / 64];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  float v[kRows][kChunks][V];
+  float ss[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    ss[r] = 0.f;
+    const int64_t row = r0 + r;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int i = (c * kThreads + threadIdx.x) * V;
+      if (row < n_rows && i < d) {
+        load16<E>(x + row * d + i, v[r][c]);
+#pragma unroll
+        for (int j = 0; j < V; ++j) ss[r] = fmaf(v[r][c][j], v[r][c][j], ss[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    ss[r] = wave_sum(ss[r]);
+    if ((threadIdx.x & 63) == 0) part[r][threadIdx.x >> 6] = ss[r];
+  }
+  __syncthreads();
+  float rs[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) tot += part[r][w];
+    rs[r] = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int i = (c * kThreads + threadIdx.x) * V;
+    if (i >= d) continue;
+    float sc[V], sh[V];
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) {
+      const float4 a = reinterpret_cast<const float4*>(scale + i)[j];
+      const float4 b = reinterpret_cast<const float4*>(shift + i)[j];
+      sc[4 * j] = 1.f + a.x; sc[4 * j + 1] = 1.f + a.y; sc[4 * j + 2] = 1.f + a.z; sc[4 * j + 3] = 1.f + a.w;
+      sh[4 * j] = b.x; sh[4 * j + 1] = b.y; sh[4 * j + 2] = b.z; sh[4 * j + 3] = b.w;
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int64_t row = r0 + r;
+      if (row >= n_rows) continue;
+      float o[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) o[j] = fmaf(v[r][c][j] * rs[r], sc[j], sh[j]);
+      if (out_tiled)  // bf16 only: 256-row x 32-column slabs (see slab_offset)
+        store16<E>(reinterpret_cast<typename E::T*>(reinterpret_cast<uint8_t*>(y) + slab_offset(row, i, d)), o);
+      else
+        store16<E>(y + row * d + i, o);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- token merge / unmerge
 // Merged row p < n_video/2 is the mean of unmerged rows 2p and 2p+1: their float32 sum is
 // exact (or, when it is not, too small a change to move the bfloat16 result), halving is exact,
@@ -315,12 +385,27 @@ hipError_t launch_norm_mod(int act, int64_t n_rows, int d, float eps, const void
                            const float* shift, const float* scale, void* y, int out_tiled,
                            hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
-  if (act == H3X_BF16)
-    norm_mod_kernel<BF16><<<dim3(n_rows), kThreads, 0, s>>>(
-        static_cast<const uint16_t*>(x), shift, scale, static_cast<uint16_t*>(y), d, eps, out_tiled);
-  else
-    norm_mod_kernel<F32><<<dim3(n_rows), kThreads, 0, s>>>(
-        static_cast<const float*>(x), shift, scale, static_cast<float*>(y), d, eps, 0);
+  constexpr int kRows = 4;
+  const unsigned grid = static_cast<unsigned>((n_rows + kRows - 1) / kRows);
+  if (act == H3X_BF16) {
+    const uint16_t* xx = static_cast<const uint16_t*>(x);
+    uint16_t* yy = static_cast<uint16_t*>(y);
+    switch ((d + kThreads * 8 - 1) / (kThreads * 8)) {
+      case 1: norm_rows_kernel<BF16, 1, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, yy, n_rows, d, eps, out_tiled); break;
+      case 2: norm_rows_kernel<BF16, 2, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, yy, n_rows, d, eps, out_tiled); break;
+      case 3: norm_rows_kernel<BF16, 3, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, yy, n_rows, d, eps, out_tiled); break;
+      case 4: norm_rows_kernel<BF16, 4, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, yy, n_rows, d, eps, out_tiled); break;
+      default: norm_mod_kernel<BF16><<<dim3(n_rows), kThreads, 0, s>>>(xx, shift, scale, yy, d, eps, out_tiled);
+    }
+  } else {
+    const float* xx = static_cast<const float*>(x);
+    float* yy = static_cast<float*>(y);
+    switch ((d + kThreads * 4 - 1) / (kThreads * 4)) {
+      case 1: norm_rows_kernel<F32, 1, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, yy, n_rows, d, eps, 0); break;
+      case 2: norm_rows_kernel<F32, 2, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, yy, n_rows, d, eps, 0); break;
+      default: norm_mod_kernel<F32><<<dim3(n_rows), kThreads, 0, s>>>(xx, shift, scale, yy, d, eps, 0);
+    }
+  }
   return hipGetLastError();
 }
 
