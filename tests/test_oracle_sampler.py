@@ -176,3 +176,117 @@ def test_reused_step_uses_cache_only():
     z1, v = sampler.denoise_step(z, text_rows(w), cache, None, None, geom, w.n_heads, "f32", 1, 20, 2, 0.95, 0.9)
     np.testing.assert_array_equal(v, cache)
     np.testing.assert_array_equal(z1, sampler.euler_update(z, sampler.sigma_delta(0.95, 0.9), cache))
+
+
+# ---------------------------------------------------------------- schedule and sampler variants
+def test_sigma_schedules():
+    for s in (1, 4, 7, 20):
+        np.testing.assert_array_equal(sampler.sigma_schedule("linear", s), sampler.sigma_grid(s))
+        np.testing.assert_array_equal(sampler.sigma_schedule("power", s, 1.0), sampler.sigma_grid(s))
+        for kind, p in (("power", 2.0), ("power", 3.0), ("power", 0.5), ("linear_terminal", 29)):
+            g = sampler.sigma_schedule(kind, s, p)
+            assert len(g) == s + 1 and g[0] == 1.0 and g[-1] == 0.0 and np.all(np.diff(g) < 0)
+    # Dyadic grids are exact: quadratic and cubic warps at S = 4.
+    np.testing.assert_array_equal(sampler.sigma_schedule("power", 4, 2.0), [1, 9 / 16, 1 / 4, 1 / 16, 0])
+    np.testing.assert_array_equal(sampler.sigma_schedule("power", 4, 3.0), [1, 27 / 64, 1 / 8, 1 / 64, 0])
+    # A few-step run on the 20-step linear base: 1, .95, .9, .85, then the terminal 0.
+    g = sampler.sigma_schedule("linear_terminal", 4, 20)
+    np.testing.assert_array_equal(g[:4], sampler.sigma_grid(20)[:4])
+    assert g[4] == 0.0
+    with pytest.raises(ValueError):
+        sampler.sigma_schedule("linear_terminal", 8, 4)
+
+
+def test_velocity_extrapolation():
+    assert sampler.extrapolation_weight(0.625, 0.75, 1.0) == np.float32(0.5)
+    assert sampler.extrapolation_weight(0.75, 0.75, 1.0) == 0
+    rng = np.random.default_rng(11)
+    va = rng.standard_normal(500).astype(np.float32)
+    vb = rng.standard_normal(500).astype(np.float32)
+    # w = 0 holds, equal velocities extrapolate to themselves.
+    np.testing.assert_array_equal(sampler.extrapolate_velocity(va, vb, 0.0), va)
+    np.testing.assert_array_equal(sampler.extrapolate_velocity(va, va, 0.37), va)
+    # One rounding of the exact w * float32(va - vb) + va.
+    w = np.float32(0.3718)
+    got = sampler.extrapolate_velocity(va, vb, w)
+    for a, b, g in zip(va[:200], vb[:200], got[:200]):
+        dd = np.float32(a) - np.float32(b)
+        exact = Fraction(float(w)) * Fraction(float(dd)) + Fraction(float(a))
+        assert Fraction(float(g)) == to_f32_exact(exact)
+    # A velocity linear in sigma (dyadic values) is reproduced exactly.
+    A = np.float32(0.375) * np.arange(-8, 8, dtype=np.float32)
+    Bv = np.float32(1.25) * np.arange(16, dtype=np.float32)
+    v_at = lambda sg: A + Bv * np.float32(sg)
+    w = sampler.extrapolation_weight(0.5, 0.75, 1.0)
+    np.testing.assert_array_equal(sampler.extrapolate_velocity(v_at(0.75), v_at(1.0), w), v_at(0.5))
+
+
+def test_cond_rows_brute_force():
+    g = Geometry(5, 3, 4, 7, 9)
+    for cf, cl in ((0, 0), (1, 0), (0, 1), (1, 1), (2, 3), (5, 0)):
+        m = sampler.cond_rows(g, cf, cl)
+        assert m.shape == (g.n_video + g.n_audio,)
+        for r in range(g.n_video + g.n_audio):
+            t = r // (g.grid_h * g.grid_w)
+            expect = r < g.n_video and (t < cf or t >= g.frames - cl)
+            assert bool(m[r]) == expect
+        assert m.sum() == min(cf + cl, g.frames) * g.grid_h * g.grid_w
+
+
+def _tiny_chain_setup():
+    from synth import TINY, block_weights, modulation, initial_state, text_rows
+    w = TINY.replace(n_blocks=4)
+    geom = Geometry(w.frames, w.grid_h, w.grid_w, w.n_audio, w.n_text)
+    blocks = [block_weights(w, b) for b in range(w.n_blocks)]
+    mods = [modulation(w, 0, b) for b in range(w.n_blocks)]
+    return w, geom, blocks, mods, initial_state(w), text_rows(w)
+
+
+def test_fixed_condition_rows_are_held():
+    w, geom, blocks, mods, z, c = _tiny_chain_setup()
+    plain = sampler.denoise_step_full(z, c, None, blocks, mods, geom, w.n_heads, "f32", 0, 4, 1, 1.0, 0.75)
+    held = sampler.denoise_step_full(z, c, None, blocks, mods, geom, w.n_heads, "f32", 0, 4, 1, 1.0, 0.75,
+                                     cond_first=1)
+    fixed = sampler.cond_rows(geom, 1, 0)
+    assert fixed.any() and not fixed.all()
+    np.testing.assert_array_equal(held[0][fixed], z[fixed])
+    np.testing.assert_array_equal(held[0][~fixed], plain[0][~fixed])
+    np.testing.assert_array_equal(held[1], plain[1])  # the DiT saw the same input
+
+
+def test_core_reuse_closed_forms():
+    w, geom, blocks, mods, z, c = _tiny_chain_setup()
+    x0 = np.concatenate([z, c]).astype(np.float64)
+    # Core fresh on every step is the plain stack, and its delta is what the core blocks add.
+    plain = sampler.dit_eval(x0, blocks, mods, geom, w.n_heads, "f32")
+    out, delta = sampler.dit_eval(x0, blocks, mods, geom, w.n_heads, "f32", core=(1, 2, True, None))
+    np.testing.assert_array_equal(out, plain)
+    x1 = dit_block(x0, blocks[0], mods[0], geom, w.n_heads)
+    x3 = dit_block(dit_block(x1, blocks[1], mods[1], geom, w.n_heads), blocks[2], mods[2], geom, w.n_heads)
+    np.testing.assert_allclose(delta, x3 - x1, rtol=0, atol=0)
+    # Outer blocks that are the identity (zero gates): a reused core adds the kept delta to the
+    # current input, whatever it is.
+    idm = [m.copy() for m in mods]
+    for b in (0, 3):
+        idm[b][2] = 0
+        idm[b][5] = 0
+    _, d_kept = sampler.dit_eval(x0, blocks, idm, geom, w.n_heads, "f32", core=(1, 2, True, None))
+    x_other = x0 * 0.5 + 0.25
+    out2, d2 = sampler.dit_eval(x_other, blocks, idm, geom, w.n_heads, "f32", core=(1, 2, False, d_kept))
+    np.testing.assert_array_equal(out2, x_other + d_kept)
+    np.testing.assert_array_equal(d2, d_kept)
+    # Through the step: core period 2 at step 1 of 4 reuses, step 2 refreshes.
+    zs, v, _, dk = sampler.denoise_step_full(z, c, None, blocks, mods, geom, w.n_heads, "f32", 0, 4, 1,
+                                             1.0, 0.75, core=(2, 1, 2, None))
+    z2, v2, _, dk2 = sampler.denoise_step_full(zs, c, v, blocks, mods, geom, w.n_heads, "f32", 1, 4, 1,
+                                               0.75, 0.5, core=(2, 1, 2, dk))
+    np.testing.assert_array_equal(dk2, dk)
+    xin = np.concatenate([zs, c]).astype(np.float64)
+    front = dit_block(xin, blocks[0], mods[0], geom, w.n_heads)
+    tail = dit_block(front + dk, blocks[3], mods[3], geom, w.n_heads)
+    np.testing.assert_array_equal(v2, tail[: geom.n_video + geom.n_audio].astype(np.float32))
+
+
+def dit_block(x, wts, mod, geom, n_heads):
+    from oracle import dit
+    return dit.block_forward(x, wts, mod, geom, n_heads)
