@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define H3X_ABI_VERSION 1
+#define H3X_ABI_VERSION 2
 
 typedef enum {
   H3X_OK = 0,
@@ -87,7 +87,7 @@ typedef struct {
   const void *s_qkv, *s_out, *s_gate_up, *s_down;
 } h3x_block_weights;
 
-/* One sampler step (host struct). */
+/* One sampler step (host struct). Zero-initialised variant fields give the plain step. */
 typedef struct {
   int32_t step, n_steps, reuse;     /* 0 <= step < n_steps, reuse >= 1 */
   float sigma, sigma_next;          /* finite; the update uses float32(sigma_next - sigma) */
@@ -96,6 +96,26 @@ typedef struct {
   const float *mod;                 /* dev [n_blocks x 6 x d] float32 modulation of this step */
   int32_t tr_first, tr_last;        /* token reduction over blocks tr_first..tr_last (0-based,
                                        inclusive); -1, -1 = off */
+  /* ---- variants (ABI 2) */
+  int32_t cond_first, cond_last;    /* fixed condition rows: the video rows of the first
+                                       cond_first and last cond_last latent frames are left
+                                       unchanged by the update (the DiT sees them as usual);
+                                       cond_first + cond_last <= frames. Pages: siami.tw
+                                       "專業音訊" (fixed condition rows in the DiT). */
+  void *v_prev;                     /* dev [(Nv + Na) x d] act type, or NULL: on fresh steps it
+                                       receives the previous content of v_cache */
+  float extrap;                     /* reused steps: v = fmaf(extrap, float32(v_cache - v_prev),
+                                       v_cache) (linear extrapolation in sigma; 0 = hold the last
+                                       fresh velocity; nonzero needs v_prev). Pages: mobbang.com
+                                       / jdon.com list of tested schedules. */
+  int32_t core_reuse;               /* 0 or 1 = off; k >= 2: blocks core_first..core_last run
+                                       only on steps fresh for period k (h3x_step_is_fresh); on
+                                       the others they are replaced by x + core_delta. Needs
+                                       reuse == 1 (the two are exclusive: siami.tw control
+                                       table) and token reduction off. */
+  int32_t core_first, core_last;    /* 0 <= core_first <= core_last < n_blocks */
+  float *core_delta;                /* dev [(Nv + Na + Nt) x d] float32: written on core-fresh
+                                       steps (x after the core - x before), read on the others */
 } h3x_step;
 
 int32_t h3x_abi_version(void);
@@ -157,6 +177,20 @@ h3x_status h3x_dit_block_forward(const h3x_block_cfg *cfg, const h3x_geom *geom,
  * velocity, -1 on invalid arguments. Pages: siami.tw control table, row "整體 denoiser 復用". */
 int32_t h3x_step_is_fresh(int32_t step, int32_t n_steps, int32_t reuse);
 
+/* Sigma grids (host): sigma_out[0..n_steps] (host float array), each value computed in double
+ * and rounded once to float. H3X_SCHED_LINEAR: 1 - i/n. H3X_SCHED_POWER: (1 - i/n)^param
+ * (2, 3: the quadratic and cubic warps). H3X_SCHED_LINEAR_TERMINAL: 1 - i/param for i < n
+ * (param = a base step count >= n), then 0: a few-step run on a longer linear base grid with
+ * one terminal step. Pages: mobbang.com / jdon.com (tested schedules), siami.tw control-table
+ * section (the few-step runs' linear base grid with a single terminal endpoint). */
+typedef enum { H3X_SCHED_LINEAR = 0, H3X_SCHED_POWER = 1, H3X_SCHED_LINEAR_TERMINAL = 2 } h3x_schedule;
+h3x_status h3x_sigma_schedule(int32_t kind, int32_t n_steps, double param, float *sigma_out);
+
+/* Extrapolation weight for h3x_step.extrap: float((s - s_a) / (s_a - s_b)) in double from the
+ * float sigmas of this step (s) and of the last two fresh steps (s_a after s_b). NaN if
+ * s_a == s_b. */
+float h3x_extrapolation_weight(float sigma, float sigma_a, float sigma_b);
+
 /* Workspace of h3x_denoise_step: the block workspace of the unmerged geometry plus two token
  * buffers (unmerged and merged). geom must be unmerged. */
 size_t h3x_step_workspace_bytes(const h3x_block_cfg *cfg, const h3x_geom *geom);
@@ -167,7 +201,9 @@ size_t h3x_step_workspace_bytes(const h3x_block_cfg *cfg, const h3x_geom *geom);
  * steps it is read. A fresh step feeds [act(z); text] through blocks 0..n_blocks-1, merging
  * video pairs by their mean before block tr_first and duplicating them back before block
  * tr_last + 1 (or after the last block). Then z <- float32(z + (sigma_next - sigma) * v),
- * rounded once. geom must be unmerged; token reduction needs an even grid_w. */
+ * rounded once, except on the fixed condition rows. The variant fields of h3x_step add
+ * linear velocity extrapolation on reused steps and core reuse. geom must be unmerged; token
+ * reduction needs an even grid_w. */
 h3x_status h3x_denoise_step(const h3x_block_cfg *cfg, const h3x_geom *geom, const h3x_step *st,
                             float *z, const void *text, void *v_cache, void *ws,
                             size_t ws_bytes, void *stream);

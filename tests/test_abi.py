@@ -7,6 +7,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 from oracle import sampler
@@ -49,7 +50,24 @@ def test_library_exports_every_declared_symbol(B):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES), set(names) ^ set(B.SIGNATURES)
-    assert L.h3x_abi_version() == 1
+    assert L.h3x_abi_version() == 2
+
+
+def test_step_struct_layout_matches_c(B, tmp_path):
+    """The ctypes mirror of h3x_step has the C compiler's field offsets and size."""
+    fields = [f for f, _ in B.Step._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("%s %zu\\n", "{f}", offsetof(h3x_step, {f}));' for f in fields)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "h3x.h"\nint main(void) {\n'
+                   + body + '\n  printf("size %zu\\n", sizeof(h3x_step));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    r = subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
+    for f in fields:
+        assert int(out[f]) == getattr(B.Step, f).offset, f
+    assert int(out["size"]) == ctypes.sizeof(B.Step)
 
 
 def _cfg(B, **kw):
@@ -119,8 +137,9 @@ def test_denoise_step_rejects_before_launch(B):
     need = L.h3x_step_workspace_bytes(ctypes.byref(c), ctypes.byref(g))
     assert need > L.h3x_block_workspace_bytes(ctypes.byref(c), ctypes.byref(g))
 
-    def call(step=0, n=4, reuse=1, sigma=1.0, sigma_next=0.75, nb=4, trf=-1, trl=-1, geom=g, ws=need):
-        st = B.Step(step, n, reuse, sigma, sigma_next, nb, blocks, FAKE, trf, trl)
+    def call(step=0, n=4, reuse=1, sigma=1.0, sigma_next=0.75, nb=4, trf=-1, trl=-1, geom=g, ws=need,
+             cf=0, cl=0, vp=None, ex=0.0, core=0, c0=0, c1=0, cd=FAKE):
+        st = B.Step(step, n, reuse, sigma, sigma_next, nb, blocks, FAKE, trf, trl, cf, cl, vp, ex, core, c0, c1, cd)
         return L.h3x_denoise_step(ctypes.byref(c), ctypes.byref(geom), ctypes.byref(st), FAKE, FAKE, FAKE,
                                   FAKE, ws, None)
 
@@ -132,6 +151,29 @@ def test_denoise_step_rejects_before_launch(B):
     assert call(trf=1, trl=2, geom=_geom(B, w=11)) == 1
     assert "even" in _last(B)
     assert call(geom=_geom(B, merged=1)) == 1
+    # Variants: condition frames within the video, extrapolation only with v_prev, core reuse
+    # exclusive with whole reuse and token reduction, inside the block range, with a buffer.
+    assert call(cf=-1) == 1 and call(cl=2, cf=2) == 1 and call(cf=4) == 1
+    assert call(step=1, reuse=2, ex=0.5) == 1 and "v_prev" in _last(B)
+    assert call(ex=math.nan) == 1 and call(vp=FAKE + 8) == 1
+    assert call(core=2, c0=1, c1=2, reuse=2) == 1 and "exclusive" in _last(B)
+    assert call(core=2, c0=1, c1=2, trf=1, trl=2) == 1
+    assert call(core=2, c0=2, c1=1) == 1 and call(core=2, c0=1, c1=4) == 1 and call(core=-1) == 1
+    assert call(core=2, c0=1, c1=2, cd=None) == 1 and call(core=2, c0=1, c1=2, cd=FAKE + 4) == 1
+
+
+def test_sigma_schedules_match_oracle(B):
+    for kind, p in (("linear", 1.0), ("power", 2.0), ("power", 3.0), ("power", 0.7), ("linear_terminal", 29.0)):
+        for n in (1, 4, 7, 20):
+            got = np.array(B.sigma_schedule(kind, n, p), np.float32)
+            np.testing.assert_array_equal(got, sampler.sigma_schedule(kind, n, p))
+    L = B.lib()
+    out = (ctypes.c_float * 9)()
+    assert L.h3x_sigma_schedule(2, 8, 4.0, out) == 1 and L.h3x_sigma_schedule(1, 8, 0.0, out) == 1
+    assert L.h3x_sigma_schedule(5, 8, 1.0, out) == 1 and L.h3x_sigma_schedule(0, 0, 1.0, out) == 1
+    for s_, a, b in ((0.625, 0.75, 1.0), (0.55, 0.6, 0.65), (0.3, 0.45, 0.5)):
+        assert np.float32(B.extrapolation_weight(s_, a, b)) == sampler.extrapolation_weight(s_, a, b)
+    assert math.isnan(B.extrapolation_weight(0.5, 0.6, 0.6))
 
 
 def test_fresh_rule_matches_oracle_and_pages(B):

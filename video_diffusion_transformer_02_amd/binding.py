@@ -72,7 +72,11 @@ class Step(ctypes.Structure):
                 ("sigma", ctypes.c_float), ("sigma_next", ctypes.c_float),
                 ("n_blocks", ctypes.c_int32), ("blocks", ctypes.POINTER(BlockWeights)),
                 ("mod", ctypes.c_void_p), ("tr_first", ctypes.c_int32),
-                ("tr_last", ctypes.c_int32)]
+                ("tr_last", ctypes.c_int32),
+                ("cond_first", ctypes.c_int32), ("cond_last", ctypes.c_int32),
+                ("v_prev", ctypes.c_void_p), ("extrap", ctypes.c_float),
+                ("core_reuse", ctypes.c_int32), ("core_first", ctypes.c_int32),
+                ("core_last", ctypes.c_int32), ("core_delta", ctypes.c_void_p)]
 
 
 class KernelTime(ctypes.Structure):
@@ -97,6 +101,8 @@ SIGNATURES = {
     "h3x_block_workspace_bytes": (_SZ, [_CFG, _GEOM]),
     "h3x_dit_block_forward": (_I32, [_CFG, _GEOM, ctypes.POINTER(BlockWeights), _P, _P, _P, _SZ, _P]),
     "h3x_step_is_fresh": (_I32, [_I32, _I32, _I32]),
+    "h3x_sigma_schedule": (_I32, [_I32, _I32, ctypes.c_double, ctypes.POINTER(ctypes.c_float)]),
+    "h3x_extrapolation_weight": (_F, [_F, _F, _F]),
     "h3x_step_workspace_bytes": (_SZ, [_CFG, _GEOM]),
     "h3x_denoise_step": (_I32, [_CFG, _GEOM, ctypes.POINTER(Step), _P, _P, _P, _P, _SZ, _P]),
     "h3x_norm_mod": (_I32, [_CFG, _I64, _P, _P, _P, _P, _P]),
@@ -243,15 +249,31 @@ def step_workspace_bytes(cfg: BlockCfg, geom: Geom) -> int:
 def denoise_step(cfg: BlockCfg, geom: Geom, step: int, n_steps: int, reuse: int, sigma: float,
                  sigma_next: float, blocks, mod: torch.Tensor | None, z: torch.Tensor,
                  text: torch.Tensor, v_cache: torch.Tensor, ws: torch.Tensor,
-                 tr_first: int = -1, tr_last: int = -1):
+                 tr_first: int = -1, tr_last: int = -1, cond_first: int = 0, cond_last: int = 0,
+                 v_prev: torch.Tensor | None = None, extrap: float = 0.0, core_reuse: int = 0,
+                 core_first: int = 0, core_last: int = 0, core_delta: torch.Tensor | None = None):
     """blocks: a ctypes array of BlockWeights (see block_array) or None on reused steps."""
     n_blocks = len(blocks) if blocks is not None else 0
     st = Step(step, n_steps, reuse, sigma, sigma_next, n_blocks,
               ctypes.cast(blocks, ctypes.POINTER(BlockWeights)) if blocks is not None else None,
-              _p(mod), tr_first, tr_last)
+              _p(mod), tr_first, tr_last, cond_first, cond_last, _p(v_prev), extrap, core_reuse,
+              core_first, core_last, _p(core_delta))
     _check(lib().h3x_denoise_step(ctypes.byref(cfg), ctypes.byref(geom), ctypes.byref(st), _p(z),
                                   _p(text), _p(v_cache), _p(ws), ws.numel(), _stream()),
            "denoise_step")
+
+
+SCHEDULES = {"linear": 0, "power": 1, "linear_terminal": 2}
+
+
+def sigma_schedule(kind: str, n_steps: int, param: float = 1.0) -> list:
+    out = (ctypes.c_float * (n_steps + 1))()
+    _check(lib().h3x_sigma_schedule(SCHEDULES[kind], n_steps, float(param), out), "sigma_schedule")
+    return list(out)
+
+
+def extrapolation_weight(sigma: float, sigma_a: float, sigma_b: float) -> float:
+    return lib().h3x_extrapolation_weight(sigma, sigma_a, sigma_b)
 
 
 def block_array(packed_blocks) -> ctypes.Array:

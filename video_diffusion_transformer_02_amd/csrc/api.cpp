@@ -1,5 +1,6 @@
 // C ABI of libh3x: argument validation, workspace layout, dispatch of the kernel launchers,
 // error reporting and optional per-kernel event timing. No device memory is allocated here.
+#include <cmath>
 #include <math.h>
 #include <string.h>
 
@@ -417,6 +418,30 @@ int32_t h3x_step_is_fresh(int32_t step, int32_t n_steps, int32_t reuse) {
   return (step % reuse == 0 || step == n_steps - 1) ? 1 : 0;
 }
 
+h3x_status h3x_sigma_schedule(int32_t kind, int32_t n_steps, double param, float* out) {
+  if (n_steps < 1 || !out) return fail(H3X_EINVAL, "sigma_schedule: need n_steps >= 1 and an output");
+  if (!std::isfinite(param)) return fail(H3X_EINVAL, "sigma_schedule: non-finite param");
+  if (kind == H3X_SCHED_POWER && !(param > 0)) return fail(H3X_EINVAL, "sigma_schedule: power needs param > 0");
+  if (kind == H3X_SCHED_LINEAR_TERMINAL && param < n_steps)
+    return fail(H3X_EINVAL, "sigma_schedule: the base step count must be >= n_steps");
+  if (kind < H3X_SCHED_LINEAR || kind > H3X_SCHED_LINEAR_TERMINAL) return fail(H3X_EINVAL, "sigma_schedule: bad kind");
+  for (int32_t i = 0; i <= n_steps; ++i) {
+    const double t = static_cast<double>(i);
+    double v;
+    if (kind == H3X_SCHED_LINEAR) v = 1.0 - t / n_steps;
+    else if (kind == H3X_SCHED_POWER) v = std::pow(1.0 - t / n_steps, param);
+    else v = i == n_steps ? 0.0 : 1.0 - t / param;
+    out[i] = static_cast<float>(v);
+  }
+  return H3X_OK;
+}
+
+float h3x_extrapolation_weight(float sigma, float sigma_a, float sigma_b) {
+  const double sa = sigma_a, sb = sigma_b;
+  if (sa == sb) return NAN;
+  return static_cast<float>((static_cast<double>(sigma) - sa) / (sa - sb));
+}
+
 size_t h3x_step_workspace_bytes(const h3x_block_cfg* c, const h3x_geom* g) {
   if (check_cfg(c) != H3X_OK || check_geom(g) != H3X_OK || g->merged) return 0;
   return step_layout(c, g, nullptr).bytes;
@@ -436,6 +461,21 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
   const int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h * g->grid_w;
   const int64_t n_state = nv + g->n_audio;
   if (!z || !v_cache || !aligned16(z) || !aligned16(v_cache)) return fail(H3X_EINVAL, "denoise_step: NULL or misaligned z / v_cache");
+  if (st_->cond_first < 0 || st_->cond_last < 0 || st_->cond_first + st_->cond_last > g->frames)
+    return fail(H3X_EINVAL, "denoise_step: need cond_first, cond_last >= 0 and their sum <= frames");
+  if (!std::isfinite(st_->extrap)) return fail(H3X_EINVAL, "denoise_step: non-finite extrap");
+  if (st_->v_prev && !aligned16(st_->v_prev)) return fail(H3X_EINVAL, "denoise_step: misaligned v_prev");
+  if (!fresh && st_->extrap != 0.0f && !st_->v_prev)
+    return fail(H3X_EINVAL, "denoise_step: extrapolation needs v_prev");
+  const bool core_on = st_->core_reuse >= 2;
+  if (st_->core_reuse < 0) return fail(H3X_EINVAL, "denoise_step: negative core_reuse");
+  if (core_on) {
+    if (st_->reuse != 1) return fail(H3X_EINVAL, "denoise_step: core reuse and whole-velocity reuse are exclusive");
+    if (st_->tr_first != -1 || st_->tr_last != -1) return fail(H3X_EINVAL, "denoise_step: core reuse needs token reduction off");
+    if (st_->core_first < 0 || st_->core_first > st_->core_last || st_->core_last >= st_->n_blocks)
+      return fail(H3X_EINVAL, "denoise_step: need 0 <= core_first <= core_last < n_blocks");
+    if (!st_->core_delta || !aligned16(st_->core_delta)) return fail(H3X_EINVAL, "denoise_step: NULL or misaligned core_delta");
+  }
   if (fresh) {
     if (st_->n_blocks < 1 || !st_->blocks || !st_->mod || !aligned16(st_->mod))
       return fail(H3X_EINVAL, "denoise_step: fresh step needs n_blocks >= 1, blocks and mod");
@@ -456,10 +496,19 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float delta = st_->sigma_next - st_->sigma;  // float32 subtraction
   const int64_t n_elems = n_state * c->d_model;
+  // Fixed condition rows: video rows of the first cond_first and last cond_last frames.
+  const int64_t per_frame = static_cast<int64_t>(g->grid_h) * g->grid_w;
+  const int64_t cond_lo = st_->cond_first * per_frame;
+  const int64_t cond_hi = (static_cast<int64_t>(g->frames) - st_->cond_last) * per_frame;
   if (!fresh) {
-    H3X_LAUNCH("euler", s, launch_euler(c->act, n_elems, z, v_cache, delta, nullptr, s));
+    const void* vp = st_->extrap != 0.0f ? st_->v_prev : nullptr;
+    H3X_LAUNCH("euler", s, launch_euler(c->act, n_elems, c->d_model, z, v_cache, vp, st_->extrap, delta, nullptr,
+                                        cond_lo, cond_hi, nv, s));
     return H3X_OK;
   }
+  // The velocity about to be replaced becomes the previous one.
+  if (st_->v_prev)
+    H3X_LAUNCH("copy", s, launch_copy(v_cache, st_->v_prev, static_cast<size_t>(n_elems) * elem_bytes(c->act), s));
   const StepWs lay = step_layout(c, g, static_cast<uint8_t*>(ws));
   h3x_geom gm = *g;
   gm.merged = 1;
@@ -469,8 +518,19 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
 
   H3X_LAUNCH("assemble", s, launch_assemble(c->act, n_state, g->n_text, c->d_model, z, text, lay.x, s));
   const size_t mod_stride = 6 * static_cast<size_t>(c->d_model);
+  const bool core_fresh = core_on && h3x_step_is_fresh(st_->step, st_->n_steps, st_->core_reuse) == 1;
+  const int64_t n_all = (n_state + g->n_text) * c->d_model;
   bool merged = false;
   for (int b = 0; b < st_->n_blocks; ++b) {
+    if (core_on && b == st_->core_first) {
+      if (core_fresh) {
+        H3X_LAUNCH("core_save", s, launch_core(c->act, 0, n_all, lay.x, st_->core_delta, s));
+      } else {  // the kept change of the core replaces its blocks
+        H3X_LAUNCH("core_apply", s, launch_core(c->act, 2, n_all, lay.x, st_->core_delta, s));
+        b = st_->core_last;
+        continue;
+      }
+    }
     if (use_tr && b == st_->tr_first) {
       H3X_LAUNCH("token_merge", s, launch_token_merge(c->act, geom_dev(*g), c->d_model, lay.x, lay.xm, s));
       merged = true;
@@ -496,10 +556,13 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
     if ((st = block_forward_impl(c, gb, &st_->blocks[b], st_->mod + b * mod_stride,
                                  merged ? lay.xm : lay.x, bw, s)) != H3X_OK)
       return st;
+    if (core_fresh && b == st_->core_last)
+      H3X_LAUNCH("core_diff", s, launch_core(c->act, 1, n_all, lay.x, st_->core_delta, s));
   }
   if (merged)
     H3X_LAUNCH("token_unmerge", s, launch_token_unmerge(c->act, geom_dev(*g), c->d_model, lay.xm, lay.x, s));
-  H3X_LAUNCH("euler", s, launch_euler(c->act, n_elems, z, lay.x, delta, v_cache, s));
+  H3X_LAUNCH("euler", s, launch_euler(c->act, n_elems, c->d_model, z, lay.x, nullptr, 0.0f, delta, v_cache,
+                                      cond_lo, cond_hi, nv, s));
   return H3X_OK;
 }
 
@@ -650,7 +713,8 @@ h3x_status h3x_euler(const h3x_block_cfg* c, int64_t n_rows, float* z, const voi
   if (!z || !v || !aligned16(z) || !aligned16(v) || (v_copy && !aligned16(v_copy)))
     return fail(H3X_EINVAL, "euler: NULL or misaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  H3X_LAUNCH("euler", s, launch_euler(c->act, n_rows * c->d_model, z, v, sigma_next - sigma, v_copy, s));
+  H3X_LAUNCH("euler", s, launch_euler(c->act, n_rows * c->d_model, c->d_model, z, v, nullptr, 0.0f, sigma_next - sigma,
+                                      v_copy, 0, 0, 0, s));
   return H3X_OK;
 }
 

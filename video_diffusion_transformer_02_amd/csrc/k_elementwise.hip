@@ -213,31 +213,91 @@ __global__ __launch_bounds__(kThreads) void unmerge_kernel(const typename E::T* 
 
 // ---------------------------------------------------------------- Euler update
 // z <- fma(delta, v, z): one rounding of the exact z + delta * v.
+// Fixed condition rows of the Euler update: video rows [0, lo) and [hi, n_video) of z.
+struct CondRows {
+  int64_t lo, hi, n_video;
+};
+
+// z += delta * v, one float32 rounding (fmaf), 4 elements per lane, except on fixed condition
+// rows. v is the fresh velocity (copied to v_copy when given) or, on reused steps with
+// v_prev, the extrapolation fmaf(w, float32(v - v_prev), v).
 template <class E>
 __global__ __launch_bounds__(kThreads) void euler_kernel(float* __restrict__ z,
                                                          const typename E::T* __restrict__ v,
-                                                         float delta,
+                                                         const typename E::T* __restrict__ v_prev,
+                                                         float w, float delta,
                                                          typename E::T* __restrict__ v_copy,
-                                                         int64_t n4) {
+                                                         int64_t n4, int d, CondRows cond) {
   for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * kThreads) {
-    float4 zz = reinterpret_cast<float4*>(z)[i];
-    float vv[4];
+    const int64_t row = (4 * i) / d;
+    float vv[4], pv[4];
     if constexpr (sizeof(typename E::T) == 4) {
       const float4 t = reinterpret_cast<const float4*>(v)[i];
       vv[0] = t.x; vv[1] = t.y; vv[2] = t.z; vv[3] = t.w;
       if (v_copy) reinterpret_cast<float4*>(v_copy)[i] = t;
+      if (v_prev) {
+        const float4 u = reinterpret_cast<const float4*>(v_prev)[i];
+        pv[0] = u.x; pv[1] = u.y; pv[2] = u.z; pv[3] = u.w;
+      }
     } else {
       const uint2 t = reinterpret_cast<const uint2*>(v)[i];
       vv[0] = __uint_as_float(t.x << 16); vv[1] = __uint_as_float(t.x & 0xffff0000u);
       vv[2] = __uint_as_float(t.y << 16); vv[3] = __uint_as_float(t.y & 0xffff0000u);
       if (v_copy) reinterpret_cast<uint2*>(v_copy)[i] = t;
+      if (v_prev) {
+        const uint2 u = reinterpret_cast<const uint2*>(v_prev)[i];
+        pv[0] = __uint_as_float(u.x << 16); pv[1] = __uint_as_float(u.x & 0xffff0000u);
+        pv[2] = __uint_as_float(u.y << 16); pv[3] = __uint_as_float(u.y & 0xffff0000u);
+      }
     }
+    if (row < cond.lo || (row >= cond.hi && row < cond.n_video)) continue;  // held condition row
+    if (v_prev) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vv[j] = fmaf(w, vv[j] - pv[j], vv[j]);
+    }
+    float4 zz = reinterpret_cast<float4*>(z)[i];
     zz.x = fmaf(delta, vv[0], zz.x);
     zz.y = fmaf(delta, vv[1], zz.y);
     zz.z = fmaf(delta, vv[2], zz.z);
     zz.w = fmaf(delta, vv[3], zz.w);
     reinterpret_cast<float4*>(z)[i] = zz;
+  }
+}
+
+// Core reuse: save (delta = x), diff (delta = x - delta) and apply (x = act(x + delta)) over
+// n4 groups of 4 elements; delta is float32.
+template <class E, int kOp>
+__global__ __launch_bounds__(kThreads) void core_kernel(typename E::T* __restrict__ x,
+                                                        float* __restrict__ delta, int64_t n4) {
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * kThreads) {
+    float xv[4];
+    if constexpr (sizeof(typename E::T) == 4) {
+      const float4 t = reinterpret_cast<const float4*>(x)[i];
+      xv[0] = t.x; xv[1] = t.y; xv[2] = t.z; xv[3] = t.w;
+    } else {
+      const uint2 t = reinterpret_cast<const uint2*>(x)[i];
+      xv[0] = __uint_as_float(t.x << 16); xv[1] = __uint_as_float(t.x & 0xffff0000u);
+      xv[2] = __uint_as_float(t.y << 16); xv[3] = __uint_as_float(t.y & 0xffff0000u);
+    }
+    float4* dp = reinterpret_cast<float4*>(delta) + i;
+    if constexpr (kOp == 0) {
+      *dp = make_float4(xv[0], xv[1], xv[2], xv[3]);
+    } else if constexpr (kOp == 1) {
+      const float4 dd = *dp;
+      *dp = make_float4(xv[0] - dd.x, xv[1] - dd.y, xv[2] - dd.z, xv[3] - dd.w);
+    } else {
+      const float4 dd = *dp;
+      const float y[4] = {xv[0] + dd.x, xv[1] + dd.y, xv[2] + dd.z, xv[3] + dd.w};
+      if constexpr (sizeof(typename E::T) == 4) {
+        reinterpret_cast<float4*>(x)[i] = make_float4(y[0], y[1], y[2], y[3]);
+      } else {
+        reinterpret_cast<uint2*>(x)[i] =
+            make_uint2(static_cast<uint32_t>(f32_to_bf16_bits(y[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(y[1])) << 16),
+                       static_cast<uint32_t>(f32_to_bf16_bits(y[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(y[3])) << 16));
+      }
+    }
   }
 }
 
@@ -438,17 +498,39 @@ hipError_t launch_token_unmerge(int act, const GeomDev& g, int d, const void* xm
   return hipGetLastError();
 }
 
-hipError_t launch_euler(int act, int64_t n_elems, float* z, const void* v, float delta,
-                        void* v_copy, hipStream_t s) {
+hipError_t launch_euler(int act, int64_t n_elems, int d, float* z, const void* v,
+                        const void* v_prev, float w, float delta, void* v_copy, int64_t cond_lo,
+                        int64_t cond_hi, int64_t n_video, hipStream_t s) {
   const int64_t n4 = n_elems / 4;
   if (n4 == 0) return hipSuccess;
   const int grid = grid_for(n4);
+  const CondRows cond{cond_lo, cond_hi, n_video};
   if (act == H3X_BF16)
-    euler_kernel<BF16><<<grid, kThreads, 0, s>>>(z, static_cast<const uint16_t*>(v), delta,
-                                                 static_cast<uint16_t*>(v_copy), n4);
+    euler_kernel<BF16><<<grid, kThreads, 0, s>>>(z, static_cast<const uint16_t*>(v),
+                                                 static_cast<const uint16_t*>(v_prev), w, delta,
+                                                 static_cast<uint16_t*>(v_copy), n4, d, cond);
   else
-    euler_kernel<F32><<<grid, kThreads, 0, s>>>(z, static_cast<const float*>(v), delta,
-                                                static_cast<float*>(v_copy), n4);
+    euler_kernel<F32><<<grid, kThreads, 0, s>>>(z, static_cast<const float*>(v),
+                                                static_cast<const float*>(v_prev), w, delta,
+                                                static_cast<float*>(v_copy), n4, d, cond);
+  return hipGetLastError();
+}
+
+hipError_t launch_core(int act, int op, int64_t n_elems, void* x, float* delta, hipStream_t s) {
+  const int64_t n4 = n_elems / 4;
+  if (n4 == 0) return hipSuccess;
+  const int grid = grid_for(n4);
+  if (act == H3X_BF16) {
+    uint16_t* xx = static_cast<uint16_t*>(x);
+    if (op == 0) core_kernel<BF16, 0><<<grid, kThreads, 0, s>>>(xx, delta, n4);
+    else if (op == 1) core_kernel<BF16, 1><<<grid, kThreads, 0, s>>>(xx, delta, n4);
+    else core_kernel<BF16, 2><<<grid, kThreads, 0, s>>>(xx, delta, n4);
+  } else {
+    float* xx = static_cast<float*>(x);
+    if (op == 0) core_kernel<F32, 0><<<grid, kThreads, 0, s>>>(xx, delta, n4);
+    else if (op == 1) core_kernel<F32, 1><<<grid, kThreads, 0, s>>>(xx, delta, n4);
+    else core_kernel<F32, 2><<<grid, kThreads, 0, s>>>(xx, delta, n4);
+  }
   return hipGetLastError();
 }
 

@@ -14,8 +14,13 @@ hipError_t launch_token_merge(int act, const GeomDev& g, int d, const void* x, v
                               hipStream_t s);
 hipError_t launch_token_unmerge(int act, const GeomDev& g, int d, const void* xm, void* x,
                                 hipStream_t s);
-hipError_t launch_euler(int act, int64_t n_elems, float* z, const void* v, float delta,
-                        void* v_copy, hipStream_t s);
+// z += delta * v on every row except the fixed condition rows [0, cond_lo) and
+// [cond_hi, n_video); v_prev != nullptr: v is extrapolated as fmaf(w, v - v_prev, v).
+hipError_t launch_euler(int act, int64_t n_elems, int d, float* z, const void* v,
+                        const void* v_prev, float w, float delta, void* v_copy, int64_t cond_lo,
+                        int64_t cond_hi, int64_t n_video, hipStream_t s);
+// Core reuse: op 0 delta = x, op 1 delta = x - delta, op 2 x = act(x + delta).
+hipError_t launch_core(int act, int op, int64_t n_elems, void* x, float* delta, hipStream_t s);
 hipError_t launch_assemble(int act, int64_t n_state, int64_t n_text, int d, const float* z,
                            const void* text, void* x, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
