@@ -193,7 +193,9 @@ def bench_denoise(args, B, torch, synth):
         gen.manual_seed(seed)
         return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std).to(torch.bfloat16)
 
-    def run(wl, packed, label):
+    def run(wl, packed, label, core=None, extrap=False, sched=("linear", 1.0), cond=(0, 0)):
+        """core: (k, first, last) core reuse; extrap: linear velocity extrapolation on reused
+        steps; sched: sigma schedule (kind, param); cond: fixed condition frames (first, last)."""
         cfg = B.BlockCfg.make(wl.d_model, wl.n_heads, wl.head_dim, wl.ffn_inner, "bf16", wl.weight)
         g = B.Geom(wl.frames, wl.grid_h, wl.grid_w, wl.n_audio, wl.n_text, 0)
         arr = B.block_array(packed)
@@ -202,17 +204,26 @@ def bench_denoise(args, B, torch, synth):
         text = synth.to_storage(synth.text_rows(wl), "bf16").cuda()
         mods = [torch.from_numpy(np.stack([synth.modulation(wl, i, b) for b in range(wl.n_blocks)])).cuda()
                 for i in range(wl.n_steps)]
-        sig = [float(np.float32(1.0 - i / wl.n_steps)) for i in range(wl.n_steps + 1)]
+        sig = B.sigma_schedule(sched[0], wl.n_steps, sched[1])
+        v_prev = torch.empty(wl.n_state, wl.d_model, dtype=torch.bfloat16, device="cuda") if extrap else None
+        delta = torch.empty(wl.n_tokens, wl.d_model, dtype=torch.float32, device="cuda") if core else None
+        fresh_steps = [i for i in range(wl.n_steps) if B.step_is_fresh(i, wl.n_steps, wl.reuse)]
 
         def schedule(times):
             z = z0.clone()
             v = torch.empty(wl.n_state, wl.d_model, dtype=torch.bfloat16, device="cuda")
             for i in range(wl.n_steps):
+                w = 0.0
+                past = [j for j in fresh_steps if j < i]
+                if extrap and i not in fresh_steps and len(past) >= 2:
+                    w = B.extrapolation_weight(sig[i], sig[past[-1]], sig[past[-2]])
                 if times is not None:
                     torch.cuda.synchronize()
                     t0 = time.perf_counter()
                 B.denoise_step(cfg, g, i, wl.n_steps, wl.reuse, sig[i], sig[i + 1], arr, mods[i], z, text, v, ws,
-                               wl.tr_first, wl.tr_last)
+                               wl.tr_first, wl.tr_last, cond_first=cond[0], cond_last=cond[1], v_prev=v_prev,
+                               extrap=w, core_reuse=core[0] if core else 0, core_first=core[1] if core else 0,
+                               core_last=core[2] if core else 0, core_delta=delta)
                 if times is not None:
                     torch.cuda.synchronize()
                     times.append((time.perf_counter() - t0) * 1e3)
@@ -230,18 +241,28 @@ def bench_denoise(args, B, torch, synth):
         reused = [t for i, t in enumerate(times) if not B.step_is_fresh(i, wl.n_steps, wl.reuse)]
         n_tok = wl.n_tokens
         nm = wl.n_video // 2 + wl.n_audio + wl.n_text
+        bf = block_flops(n_tok, wl.d_model, wl.ffn_inner)
         if wl.tr_first >= 0:
             n_red = wl.tr_last - wl.tr_first + 1
-            eval_flops = (wl.n_blocks - n_red) * block_flops(n_tok, wl.d_model, wl.ffn_inner) + \
-                n_red * block_flops(nm, wl.d_model, wl.ffn_inner)
+            eval_flops = (wl.n_blocks - n_red) * bf + n_red * block_flops(nm, wl.d_model, wl.ffn_inner)
         else:
-            eval_flops = wl.n_blocks * block_flops(n_tok, wl.d_model, wl.ffn_inner)
+            eval_flops = wl.n_blocks * bf
         fresh_ms = float(np.mean(fresh))
         res = {"ms_per_step": round(total / wl.n_steps, 3), "total_ms": round(total, 2),
                "fresh_steps": len(fresh), "ms_per_fresh_step": round(fresh_ms, 3),
                "ms_per_reused_step": round(float(np.mean(reused)), 4) if reused else None,
-               "tflops_fresh": round(eval_flops / fresh_ms / 1e9, 1),
                "finite": bool(torch.isfinite(z).all().item())}
+        if core:
+            k, first, last = core
+            core_fresh = [B.step_is_fresh(i, wl.n_steps, k) for i in range(wl.n_steps)]
+            n_core = last - first + 1
+            flops = sum(eval_flops if cf else (wl.n_blocks - n_core) * bf for cf in core_fresh)
+            res["core_fresh_steps"] = sum(core_fresh)
+            res["tflops"] = round(flops / total / 1e9, 1)
+        else:
+            res["tflops_fresh"] = round(eval_flops / fresh_ms / 1e9, 1)
+        if sched[0] != "linear":
+            res["sigma"] = [round(x, 4) for x in sig]
         log(f"[bench] {label}: {res}")
         return res
 
@@ -259,6 +280,13 @@ def bench_denoise(args, B, torch, synth):
     torch.cuda.synchronize()
     out["denoise_45blk_20step_reuse2"] = run(wl, packed, "45 blocks, 20 steps, reuse 2")
     out["denoise_45blk_20step_reuse2_tr10_34"] = run(synth.DENOISE45_TR, packed, "same + token reduction 10..34")
+    out["denoise_45blk_20step_reuse2_extrap"] = run(wl, packed, "reuse 2 with linear velocity extrapolation",
+                                                    extrap=True)
+    out["denoise_45blk_20step_core4_10_34"] = run(wl.replace(reuse=1), packed, "core reuse 4 over blocks 10..34",
+                                                  core=(4, 10, 34))
+    out["denoise_45blk_4step_linear_terminal_cond1"] = run(
+        wl.replace(n_steps=4, reuse=1), packed, "4 steps, linear base grid of 20 + terminal step, first frame fixed",
+        sched=("linear_terminal", 20.0), cond=(1, 0))
     del packed
     torch.cuda.empty_cache()
 
