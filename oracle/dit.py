@@ -95,13 +95,16 @@ def _w(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
 
-def block_forward(x, w: dict, mod, geom: Geometry, n_heads: int, rows=None) -> np.ndarray:
+def block_forward(x, w: dict, mod, geom: Geometry, n_heads: int, rows=None, act_quant=None) -> np.ndarray:
     """Block output x2 for the rows ``rows`` (all rows if None).
 
     x [N, d] is the block input (all N rows are needed: every query attends to every key).
     w holds unpacked weights: qkv [3d, d], out [d, d], gate [F, d], up [F, d], down [d, F].
     mod [6, d] holds shift1, scale1, gate1, shift2, scale2, gate2.
+    act_quant: None, or a function applied to each projection's input activation (the W8A8
+    path passes the per-row int8 quantise-dequantise of the stored value).
     """
+    aq = (lambda a: a) if act_quant is None else act_quant
     x = np.asarray(x, np.float64)
     n, d = x.shape
     if n != geom.n_tokens:
@@ -112,16 +115,16 @@ def block_forward(x, w: dict, mod, geom: Geometry, n_heads: int, rows=None) -> n
     wqkv = _w(w["qkv"])
     wq, wk, wv = wqkv[0:d], wqkv[d:2 * d], wqkv[2 * d:3 * d]
 
-    y = rms_norm_mod(x, shift1, scale1)
+    y = aq(rms_norm_mod(x, shift1, scale1))
     pos, rot = geom.positions()
     q = rope(y[rows] @ wq.T, pos[rows], rot[rows], n_heads)
     k = rope(y @ wk.T, pos, rot, n_heads)
     v = y @ wv.T
-    o = attention(q, k, v, n_heads)
+    o = aq(attention(q, k, v, n_heads))
     x1 = x[rows] + gate1 * (o @ _w(w["out"]).T)
 
-    y2 = rms_norm_mod(x1, shift2, scale2)
-    h = silu(y2 @ _w(w["gate"]).T) * (y2 @ _w(w["up"]).T)
+    y2 = aq(rms_norm_mod(x1, shift2, scale2))
+    h = aq(silu(y2 @ _w(w["gate"]).T) * (y2 @ _w(w["up"]).T))
     return x1 + gate2 * (h @ _w(w["down"]).T)
 
 

@@ -162,8 +162,10 @@ def test_silu_values():
 
 
 # ---------------------------------------------------------------- whole block
-def brute_block(x, w, mod, geom, nh):
-    """Loop-level block from the stated definitions (no shared code with the oracle)."""
+def brute_block(x, w, mod, geom, nh, act_quant=None):
+    """Loop-level block from the stated definitions (no shared code with the oracle).
+    act_quant, if given, maps one projection-input row to its quantised values."""
+    aq = act_quant or (lambda row: row)
     n, d = x.shape
     dh = d // nh
     f = w["gate"].shape[0]
@@ -201,7 +203,7 @@ def brute_block(x, w, mod, geom, nh):
                 base += sizes[a]
         return out
 
-    ys = [norm(list(x[i]), shift1, scale1) for i in range(n)]
+    ys = [aq(norm(list(x[i]), shift1, scale1)) for i in range(n)]
     wq, wk, wv = w["qkv"][:d], w["qkv"][d:2 * d], w["qkv"][2 * d:]
     qs = [rot(matvec(wq, ys[i]), i) for i in range(n)]
     ks = [rot(matvec(wk, ys[i]), i) for i in range(n)]
@@ -209,12 +211,12 @@ def brute_block(x, w, mod, geom, nh):
     att = brute_attention(np.array(qs), np.array(ks), np.array(vs), nh)
     out = np.zeros((n, d))
     for i in range(n):
-        ao = matvec(w["out"], list(att[i]))
+        ao = matvec(w["out"], aq(list(att[i])))
         x1 = [x[i, c] + gate1[c] * ao[c] for c in range(d)]
-        y2 = norm(x1, shift2, scale2)
+        y2 = aq(norm(x1, shift2, scale2))
         g = matvec(w["gate"], y2)
         u = matvec(w["up"], y2)
-        hmid = [g[j] / (1 + math.exp(-g[j])) * u[j] for j in range(f)]
+        hmid = aq([g[j] / (1 + math.exp(-g[j])) * u[j] for j in range(f)])
         mo = matvec(w["down"], hmid)
         out[i] = [x1[c] + gate2[c] * mo[c] for c in range(d)]
     return out
