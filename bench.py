@@ -9,9 +9,13 @@ Default run (one GPU):
     its launches on the launch stream inside the timed region.
   * cpu_baseline: the float64 NumPy oracle on a bounded sample of the same block (all K/V rows,
     a few query rows), on this host's cores.
+  * block_w8a8: the same block with int8 weights and per-row int8 activations (int8 matrix
+    cores, int32 accumulation); its GEMM rates are against the dense int8 peak.
   * denoise: ms per sampler step for the 45-block / 20-step / reuse-2 schedule, the same with
-    token reduction over blocks 10..34, and the 50-block int8-weight 4-step schedule at the
-    6 x 30 x 54 grid (synthetic weights drawn on the GPU).
+    token reduction over blocks 10..34, velocity extrapolation, core reuse, a four-step
+    schedule with a fixed first frame, and the 50-block 4-step schedule at the 6 x 30 x 54 grid
+    with int8 weights (W8A16) and with int8 weights and activations (W8A8); synthetic weights
+    drawn on the GPU.
 Inputs are synthetic and seeded (see synth/).
 """
 from __future__ import annotations
@@ -28,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "DiT block TFLOP/s (% MFMA peak) + ms per denoise step, 512×512×22f"
 
@@ -45,6 +50,9 @@ def parse():
                    help="counter summary with the dominant kernel's HBM bytes per launch "
                         "(default: the one under profiles/)")
     p.add_argument("--only-block", action="store_true", help="block timing only (for profilers)")
+    p.add_argument("--block-weight", default="bf16", choices=["bf16", "i8", "i8a8"],
+                   help="weight type of the block timed with --only-block")
+    p.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 block and schedule")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run a 1 GiB device copy (byte-counter calibration)")
     return p.parse_args()
@@ -82,12 +90,12 @@ def measured_traffic(path):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def bench_block(args, B, torch, synth):
+def bench_block(args, B, torch, synth, weight="bf16"):
     w = synth.BLOCK
-    cfg = B.BlockCfg.make(w.d_model, w.n_heads, w.head_dim, w.ffn_inner, "bf16", "bf16")
+    cfg = B.BlockCfg.make(w.d_model, w.n_heads, w.head_dim, w.ffn_inner, "bf16", weight)
     g = B.Geom(w.frames, w.grid_h, w.grid_w, w.n_audio, w.n_text, 0)
     n, d, f = g.n_tokens, w.d_model, w.ffn_inner
-    log(f"[bench] block workload: N={n} d={d} F={f} heads={w.n_heads}x{w.head_dim}")
+    log(f"[bench] block workload: N={n} d={d} F={f} heads={w.n_heads}x{w.head_dim} weights={weight}")
     raw = synth.block_weights(w, 0)
     dev = {k: synth.to_storage(v, "bf16").cuda() for k, v in raw.items()}
     pb = B.pack_block(cfg, dev)
@@ -122,6 +130,8 @@ def bench_block(args, B, torch, synth):
         torch.cuda.synchronize()
         del src, dst
     kern = {}
+    # Projections multiply int8 by int8 in the W8A8 block: their rates are against that peak.
+    gemm_peak = PEAK_INT8_TOPS if weight == "i8a8" else PEAK_BF16_TFLOPS
     kflops = {
         "gemm_qkv_rope": gemm_flops(n, 3 * d, d),
         "attention": 4.0 * n * n * d,
@@ -133,19 +143,22 @@ def bench_block(args, B, torch, synth):
         avg = total_ms / launches
         e = {"launches": launches, "avg_ms": round(avg, 5)}
         if name in kflops:
+            peak = PEAK_BF16_TFLOPS if name == "attention" else gemm_peak
             e["tflops"] = round(kflops[name] / avg / 1e9, 1)
-            e["frac_peak"] = round(kflops[name] / avg / 1e9 / PEAK_BF16_TFLOPS, 4)
+            e["frac_peak"] = round(kflops[name] / avg / 1e9 / peak, 4)
         if name == "norm_mod":
             e["gbs"] = round(2.0 * n * d * 2 / avg / 1e6, 1)
+        if name == "norm_mod_quant":  # bf16 row in, int8 codes + a float32 scale per row out
+            e["gbs"] = round((3.0 * n * d + 4 * n) / avg / 1e6, 1)
         kern[name] = e
         log(f"[bench]   {name:22s} {avg:8.4f} ms x{launches} {e.get('tflops', '')}")
     dom = "gemm_gate_up_swiglu"
     dom_ms = kern[dom]["avg_ms"]
     achieved = kflops[dom] / dom_ms / 1e9
-    traffic = measured_traffic(args.traffic)
-    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": dom_ms}
+    traffic = measured_traffic(args.traffic) if weight == "bf16" else None
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": gemm_peak,
+            "unit": "TFLOP/s" if weight != "i8a8" else "TOP/s", "frac": round(achieved / gemm_peak, 4),
+            "traffic": traffic, "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": dom_ms}
     state = {"raw": raw, "mod": mod, "x": x_host, "w": w}
     return ms, flops, kern, roof, state
 
@@ -304,6 +317,23 @@ def bench_denoise(args, B, torch, synth):
     out["int8w_50blk_4step_6x30x54"] = run(wl, packed, "50 blocks int8, 4 steps")
     del packed
     torch.cuda.empty_cache()
+    if args.no_w8a8:
+        return out
+
+    # The same 50 blocks with int8 weights and per-row int8 activations.
+    wl = synth.INT8_50.replace(name="w8a8_50blk_4step_6x30x54", weight="i8a8")
+    cfg = B.BlockCfg.make(wl.d_model, wl.n_heads, wl.head_dim, wl.ffn_inner, "bf16", "i8a8")
+    packed = []
+    for b in range(wl.n_blocks):
+        wts = {"qkv": rand_bf16((3 * d, d), 0.02, 1000 + 5 * b), "out": rand_bf16((d, d), 0.02, 1001 + 5 * b),
+               "gate": rand_bf16((f, d), 0.02, 1002 + 5 * b), "up": rand_bf16((f, d), 0.02, 1003 + 5 * b),
+               "down": rand_bf16((d, f), 0.02, 1004 + 5 * b)}
+        packed.append(B.pack_block(cfg, wts))
+        del wts
+    torch.cuda.synchronize()
+    out["w8a8_50blk_4step_6x30x54"] = run(wl, packed, "50 blocks W8A8, 4 steps")
+    del packed
+    torch.cuda.empty_cache()
     return out
 
 
@@ -320,10 +350,16 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     B.lib()
-    ms, flops, kern, roof, state = bench_block(args, B, torch, synth)
     if args.only_block:
-        print(json.dumps({"ms_per_step": ms, "kernels": kern}))
+        ms, flops, kern, roof, state = bench_block(args, B, torch, synth, args.block_weight)
+        print(json.dumps({"ms_per_step": ms, "weights": args.block_weight, "kernels": kern}))
         return
+    ms, flops, kern, roof, state = bench_block(args, B, torch, synth)
+    w8a8 = None
+    if not args.no_w8a8:
+        ms8, _, kern8, roof8, _ = bench_block(args, B, torch, synth, "i8a8")
+        w8a8 = {"ms_per_step": round(ms8, 4), "tops": round(flops / ms8 / 1e9, 2),
+                "speedup_vs_bf16": round(ms / ms8, 3), "dominant": roof8, "kernels": kern8}
     denoise = None if args.no_denoise else bench_denoise(args, B, torch, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, state)
     w = synth.BLOCK
@@ -347,6 +383,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kern,
+        "block_w8a8": w8a8,
         "denoise": denoise,
     }
     print(json.dumps(line))

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define H3X_ABI_VERSION 2
+#define H3X_ABI_VERSION 3
 
 typedef enum {
   H3X_OK = 0,
@@ -51,7 +51,16 @@ typedef enum {
   H3X_EHIP = 4        /* a HIP launch or runtime call failed */
 } h3x_status;
 
-typedef enum { H3X_F32 = 0, H3X_BF16 = 1, H3X_I8 = 2 } h3x_dtype;
+/* H3X_I8A8 (weights only): the int8 weights of H3X_I8 (same codes and scales, another packed
+ * layout) multiplied by int8 activations: every projection input (the normalised rows, the
+ * attention output and the SwiGLU product), as stored in bfloat16, is quantised per row with a
+ * float32 scale (a = max |x|; inv = 127 / a and s = a / 127 as IEEE float32 divisions;
+ * q = clamp(rint(x * inv), -127, 127); a == 0 or an infinite inv gives s = 0 and zero codes),
+ * the products are summed exactly in int32 and scaled by s_row * s_col in float32. Pages:
+ * jdon.com "选配还是选速" (an experimental int8 FC2 with one activation scale per row) and the
+ * W8A8 remark on arex-research.com, "一个 MiniMax 工程师的 Redis 启蒙"; here applied to all four
+ * projections. */
+typedef enum { H3X_F32 = 0, H3X_BF16 = 1, H3X_I8 = 2, H3X_I8A8 = 3 } h3x_dtype;
 
 typedef enum {
   H3X_W_QKV = 0,     /* [3d x d]: rows Q | K | V, each head-major */
@@ -62,12 +71,13 @@ typedef enum {
 
 /* Shape and numeric types of one block. Supported combinations:
  *   act F32  + weight F32  : head_dim 64 or 128, d_model % 64 == 0, ffn_inner % 64 == 0;
- *   act BF16 + weight BF16 or I8 : head_dim 128, d_model % 256 == 0, ffn_inner % 128 == 0.
+ *   act BF16 + weight BF16 or I8 : head_dim 128, d_model % 256 == 0, ffn_inner % 128 == 0;
+ *   act BF16 + weight I8A8       : as BF16, and d_model <= 8192, ffn_inner <= 32768.
  * d_model must equal n_heads * head_dim. norm_eps > 0 (1e-6), rope_theta > 1 (10000). */
 typedef struct {
   int32_t d_model, n_heads, head_dim, ffn_inner;
   int32_t act;    /* h3x_dtype of activations: H3X_F32 or H3X_BF16 */
-  int32_t weight; /* h3x_dtype of weights: H3X_F32, H3X_BF16 or H3X_I8 */
+  int32_t weight; /* h3x_dtype of weights: H3X_F32, H3X_BF16, H3X_I8 or H3X_I8A8 */
   float norm_eps;
   float rope_theta;
 } h3x_block_cfg;
@@ -80,7 +90,8 @@ typedef struct {
 } h3x_geom;
 
 /* Packed weights of one block (device pointers, produced by h3x_pack_weights or
- * h3x_pack_int8_weights). For H3X_I8 the s_* pointers hold one bfloat16 scale per packed row;
+ * h3x_pack_int8_weights). For H3X_I8 and H3X_I8A8 the s_* pointers hold one bfloat16 scale per
+ * packed row;
  * for F32 / BF16 weights they must be NULL. */
 typedef struct {
   const void *qkv, *out, *gate_up, *down;
@@ -136,7 +147,10 @@ int64_t h3x_geom_tokens(const h3x_geom *geom);
  * packed row rr = r % 256 holds 64 (BF16) or 32 (I8) bytes made of 16-byte chunks, chunk q of
  * the row stored at position q ^ ((rr >> 2) & 3) (BF16) or q ^ ((rr >> 3) & 1) (I8). This is
  * the order in which the matrix-core GEMM keeps one 32-wide K step of a 256-row tile in LDS.
- * Packed size in bytes for the cfg's weight type (I8: the codes; scales are
+ * I8A8 codes use the BF16 byte layout with 64 codes per slab row: slab (r / 256, c / 64) at
+ * ((r / 256) * (cols / 64) + c / 64) * 16384, row rr holding 64 bytes in four 16-byte chunks
+ * placed at q ^ ((rr >> 2) & 3) (one 64-wide K step of the int8 GEMM).
+ * Packed size in bytes for the cfg's weight type (I8, I8A8: the codes; scales are
  * h3x_packed_scale_count() bfloat16 values in packed row order). */
 size_t h3x_packed_weight_bytes(const h3x_block_cfg *cfg, int32_t kind);
 int64_t h3x_packed_rows(const h3x_block_cfg *cfg, int32_t kind);
@@ -153,7 +167,8 @@ h3x_status h3x_pack_weights(const h3x_block_cfg *cfg, int32_t kind, const void *
  * s = bf16(a / 127) (IEEE float32 division, round to nearest even, then round to bfloat16);
  * s == 0 (underflow) gives zero codes; else q = clamp(rint(W / s), -127, 127) with an IEEE
  * float32 division by the stored s. Pages: 21cto.com "M5 Max 生产环境实测数据" item 4; siami.tw
- * "2. 數據會說話". cfg->weight must be H3X_I8 (cfg->act H3X_BF16). */
+ * "2. 數據會說話". cfg->weight must be H3X_I8 or H3X_I8A8 (cfg->act H3X_BF16); the two differ
+ * only in the order in which the codes are stored. */
 h3x_status h3x_pack_int8_weights(const h3x_block_cfg *cfg, int32_t kind, const void *w_bf16,
                                  void *q_packed, void *scale_bf16, void *stream);
 

@@ -65,6 +65,28 @@ h3x_status h3x_linear_swiglu(const h3x_block_cfg *cfg, int64_t m, const void *y2
 h3x_status h3x_linear_f32out(const h3x_block_cfg *cfg, int32_t kind, int64_t m, const void *a,
                              const void *w, const void *s, float *out, void *stream);
 
+/* W8A8 activations (the per-row rule documented with H3X_I8A8 in h3x.h). Codes are stored as
+ * slabs of 256 rows x 64 codes in the I8A8 weight layout (slab (r / 256, c / 64) at
+ * ((r / 256) * (cols / 64) + c / 64) * 16384, row rr = r % 256 holding four 16-byte chunks at
+ * q ^ ((rr >> 2) & 3)); rows m .. round_up(m, 256) - 1 of a slab are left as they were.
+ * quant_rows: a (dev [m x cols] bfloat16, row-major) -> q (dev, round_up(m, 256) * cols bytes),
+ * s (dev float32 [m]); 0 < cols <= 32768, cols % 64 == 0.
+ * norm_mod_quant: the modulated RMSNorm of h3x_norm_mod (bfloat16, cfg->weight I8A8), rounded to
+ * bfloat16, then quantised as above (cols = d_model). */
+h3x_status h3x_quant_rows(int64_t m, int64_t cols, const void *a, void *q, float *s, void *stream);
+h3x_status h3x_norm_mod_quant(const h3x_block_cfg *cfg, int64_t n_rows, const void *x,
+                              const float *shift, const float *scale, void *q, float *s,
+                              void *stream);
+
+/* out (dev [m x packed_rows] float32)[r][c] = float(sum_k qa[r][k] w[c][k]) * sa[r] * sw[c]
+ * for an I8A8 cfg: qa, sa as written by h3x_quant_rows (qa holding round_up(m, 256) rows, sa
+ * round_up(m, 256) entries: the GEMM reads whole 256-row tiles; the values of rows past m
+ * only reach discarded outputs), w and sw from h3x_pack_int8_weights. The integer sums are
+ * exact. The other kernel-level projections return H3X_ENOTSUP for I8A8 configs. */
+h3x_status h3x_linear_a8_f32out(const h3x_block_cfg *cfg, int32_t kind, int64_t m,
+                                const void *qa, const float *sa, const void *w, const void *sw,
+                                float *out, void *stream);
+
 /* Token reduction (jdon.com, "330亿参数是什么概念"; siami.tw control table, row
  * "Token 縮減"). geom is the unmerged geometry. merge: x [N x d] -> xm [N' x d], video pair
  * (2p, 2p+1) -> row p = their mean rounded once to the act type; audio and text rows copied.

@@ -126,8 +126,10 @@ def euler_update(z, delta, v) -> np.ndarray:
 
 
 def dit_eval(x0, blocks, mods, geom: Geometry, n_heads: int, act: str,
-             tr_first: int = -1, tr_last: int = -1, core=None):
+             tr_first: int = -1, tr_last: int = -1, core=None, act_quant=None):
     """Run the block stack on x0 [N, d] with optional token reduction; float64 output [N, d].
+
+    act_quant: passed to every block (the W8A8 activation hook of dit.block_forward).
 
     core: None, or (first, last, fresh, delta): with fresh the core blocks run and
     ``x_after - x_before`` is returned as the new delta; otherwise they are replaced by
@@ -150,14 +152,14 @@ def dit_eval(x0, blocks, mods, geom: Geometry, n_heads: int, act: str,
             x_in = x
             if fresh:
                 for bb in range(first, last + 1):
-                    x = dit.block_forward(x, blocks[bb], mods[bb], g, n_heads)
+                    x = dit.block_forward(x, blocks[bb], mods[bb], g, n_heads, act_quant=act_quant)
                 delta_out = x - x_in
             else:
                 x = x_in + np.asarray(delta, np.float64)
                 delta_out = np.asarray(delta, np.float64)
             b = last + 1
             continue
-        x = dit.block_forward(x, blocks[b], mods[b], g, n_heads)
+        x = dit.block_forward(x, blocks[b], mods[b], g, n_heads, act_quant=act_quant)
         b += 1
     if g.merged:
         x = tokred.unmerge(x, g.as_unmerged())
@@ -167,7 +169,8 @@ def dit_eval(x0, blocks, mods, geom: Geometry, n_heads: int, act: str,
 def denoise_step_full(z, c, v_cache, blocks, mods, geom: Geometry, n_heads: int, act: str,
                       step: int, n_steps: int, reuse: int, sigma: float, sigma_next: float,
                       tr_first: int = -1, tr_last: int = -1, cond_first: int = 0,
-                      cond_last: int = 0, v_prev=None, extrap: float = 0.0, core=None):
+                      cond_last: int = 0, v_prev=None, extrap: float = 0.0, core=None,
+                      act_quant=None):
     """One sampler step with every variant. Returns (z_next, v_cache, v_prev, core_delta).
 
     z [Nv+Na, d] float32; c [Nt, d] text rows (values of the act type); v_cache, v_prev: the
@@ -180,11 +183,12 @@ def denoise_step_full(z, c, v_cache, blocks, mods, geom: Geometry, n_heads: int,
         x0 = np.concatenate([round_storage(z, act).astype(np.float64),
                              np.asarray(c, np.float64)], axis=0)
         if core is None:
-            out = dit_eval(x0, blocks, mods, geom, n_heads, act, tr_first, tr_last)
+            out = dit_eval(x0, blocks, mods, geom, n_heads, act, tr_first, tr_last, act_quant=act_quant)
         else:
             k, first, last, delta = core
             out, core_delta = dit_eval(x0, blocks, mods, geom, n_heads, act, tr_first, tr_last,
-                                       core=(first, last, is_fresh(step, n_steps, k), delta))
+                                       core=(first, last, is_fresh(step, n_steps, k), delta),
+                                       act_quant=act_quant)
         v_prev_next = v_cache
         v = round_storage(out[:n_state], act)
         v_cache_next = v

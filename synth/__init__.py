@@ -44,7 +44,7 @@ class Workload:
     n_text: int
     n_blocks: int
     act: str  # "f32" or "bf16": storage type of activations (and of master weights)
-    weight: str  # "f32", "bf16" or "i8"
+    weight: str  # "f32", "bf16", "i8" (int8 weights) or "i8a8" (int8 weights and activations)
     n_steps: int = 1
     reuse: int = 1
     tr_first: int = -1

@@ -60,7 +60,7 @@ def packed_block(w: synth.Workload, b: int):
     vals, dev = master_weights(w, b)
     cfg = binding_cfg(w)
     pb = B.pack_block(cfg, dev)
-    if w.weight == "i8":
+    if w.weight in ("i8", "i8a8"):
         deq = {}
         for name in vals:
             q, s = quant.pack_int8(vals[name].astype(np.float32))

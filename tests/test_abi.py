@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(B):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES), set(names) ^ set(B.SIGNATURES)
-    assert L.h3x_abi_version() == 2
+    assert L.h3x_abi_version() == 3
 
 
 def test_step_struct_layout_matches_c(B, tmp_path):
@@ -91,7 +91,9 @@ def test_cfg_validation(B):
         (dict(d_model=500), 1), (dict(head_dim=64), 1), (dict(head_dim=64, n_heads=8), 2),
         (dict(ffn_inner=700), 2),
         (dict(act="f32"), 2), (dict(act="f32", weight="f32", head_dim=32, n_heads=16), 2),
-        (dict(norm_eps=0.0), 1), (dict(rope_theta=1.0), 1),
+        (dict(norm_eps=0.0), 1), (dict(rope_theta=1.0), 1), (dict(weight=7), 1),
+        (dict(act="f32", weight="i8a8"), 2),
+        (dict(weight="i8a8", d_model=8448, n_heads=66), 2), (dict(weight="i8a8", ffn_inner=32896), 2),
     ]
     for kw, status in bad:
         c = _cfg(B, **kw)
@@ -205,6 +207,28 @@ def test_workspace_and_packing_sizes(B):
     assert L.h3x_packed_weight_bytes(ctypes.byref(c8), 3) == 6144 * 24576
     assert L.h3x_packed_scale_count(ctypes.byref(c8), 2) == 2 * 24576
     assert L.h3x_packed_weight_bytes(ctypes.byref(c8), 9) == 0
+    # W8A8: the same codes and scales, plus one int8 code per projection-input element and a
+    # float32 scale per row ([Npad x max(d, F)] bytes + 4 Npad).
+    ca = _cfg(B, d_model=6144, n_heads=48, ffn_inner=24576, weight="i8a8")
+    assert L.h3x_packed_weight_bytes(ctypes.byref(ca), 3) == 6144 * 24576
+    assert L.h3x_packed_scale_count(ctypes.byref(ca), 2) == 2 * 24576
+    wa = L.h3x_block_workspace_bytes(ctypes.byref(ca), ctypes.byref(g))
+    assert wa - ws == 6912 * 24576 + 6912 * 4
+
+
+def test_w8a8_kernel_level_contract(B):
+    """I8A8 projections take quantised activations: the bfloat16-input entry points refuse."""
+    L = B.lib()
+    c = _cfg(B, weight="i8a8")
+    assert L.h3x_linear_f32out(ctypes.byref(c), 1, 4, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.h3x_linear_residual(ctypes.byref(c), 1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.h3x_linear_swiglu(ctypes.byref(c), 4, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.h3x_quant_rows(4, 100, FAKE, FAKE, FAKE, None) == 1
+    assert L.h3x_quant_rows(4, 32832, FAKE, FAKE, FAKE, None) == 1
+    assert L.h3x_norm_mod_quant(ctypes.byref(_cfg(B, weight="i8")), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.h3x_linear_a8_f32out(ctypes.byref(_cfg(B)), 1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.h3x_linear_a8_f32out(ctypes.byref(c), 5, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.h3x_linear_a8_f32out(ctypes.byref(c), 1, 4, FAKE, None, FAKE, FAKE, FAKE, None) == 1
 
 
 def test_status_strings(B):

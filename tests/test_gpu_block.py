@@ -29,7 +29,7 @@ def _tol(wl):
         # about |s| 2^-8, which shifts softmax weights by a few percent. Checked tighter against
         # the storage-rounded reference below.
         return 3e-2
-    return TOL["i8"] if wl.weight == "i8" else TOL[wl.act]
+    return TOL["i8"] if wl.weight in ("i8", "i8a8") else TOL[wl.act]
 
 
 def branch_bound(wl, x, ref):

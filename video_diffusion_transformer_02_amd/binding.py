@@ -17,9 +17,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libh3x.so")
 _LIB = None
 
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, I8A8 = 0, 1, 2, 3
 W_QKV, W_OUT, W_GATE_UP, W_DOWN = 0, 1, 2, 3
-DTYPES = {"f32": F32, "bf16": BF16, "i8": I8}
+DTYPES = {"f32": F32, "bf16": BF16, "i8": I8, "i8a8": I8A8}
 TORCH_ACT = {F32: torch.float32, BF16: torch.bfloat16}
 
 
@@ -36,7 +36,7 @@ class BlockCfg(ctypes.Structure):
     @classmethod
     def make(cls, d_model, n_heads, head_dim, ffn_inner, act="bf16", weight="bf16",
              norm_eps=1e-6, rope_theta=10000.0):
-        return cls(d_model, n_heads, head_dim, ffn_inner, DTYPES[act], DTYPES[weight],
+        return cls(d_model, n_heads, head_dim, ffn_inner, DTYPES.get(act, act), DTYPES.get(weight, weight),
                    norm_eps, rope_theta)
 
     @property
@@ -114,6 +114,9 @@ SIGNATURES = {
     "h3x_linear_residual": (_I32, [_CFG, _I32, _I64, _P, _P, _P, _P, _P, _P]),
     "h3x_linear_swiglu": (_I32, [_CFG, _I64, _P, _P, _P, _P, _P]),
     "h3x_linear_f32out": (_I32, [_CFG, _I32, _I64, _P, _P, _P, _P, _P]),
+    "h3x_quant_rows": (_I32, [_I64, _I64, _P, _P, _P, _P]),
+    "h3x_norm_mod_quant": (_I32, [_CFG, _I64, _P, _P, _P, _P, _P, _P]),
+    "h3x_linear_a8_f32out": (_I32, [_CFG, _I32, _I64, _P, _P, _P, _P, _P, _P]),
     "h3x_token_merge": (_I32, [_CFG, _GEOM, _P, _P, _P]),
     "h3x_token_unmerge": (_I32, [_CFG, _GEOM, _P, _P, _P]),
     "h3x_euler": (_I32, [_CFG, _I64, _P, _P, _F, _F, _P, _P]),
@@ -212,7 +215,7 @@ def pack_block(cfg: BlockCfg, w: dict) -> PackedBlock:
     gu = torch.cat([w["gate"], w["up"]], dim=0)
     srcs = {"qkv": (W_QKV, w["qkv"]), "out": (W_OUT, w["out"]), "gate_up": (W_GATE_UP, gu),
             "down": (W_DOWN, w["down"])}
-    if cfg.weight == I8:
+    if cfg.weight in (I8, I8A8):
         fields = {}
         for name, (kind, t) in srcs.items():
             q, s = pack_int8_weights(cfg, kind, t.contiguous())
@@ -376,3 +379,29 @@ def profile_end(max_entries: int = 64) -> dict:
     if n < 0:
         raise H3xError(lib().h3x_last_error().decode())
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}
+
+
+def quant_rows(a, q=None, s=None):
+    """Per-row int8 codes (slabs of 256 rows x 64 codes, flat int8 tensor of pad_rows(m) * cols
+    bytes) and float32 scales [pad_rows(m)] of a bfloat16 [m x cols] tensor."""
+    m, cols = a.shape
+    q = torch.zeros(pad_rows(m) * cols, dtype=torch.int8, device=a.device) if q is None else q
+    s = torch.zeros(pad_rows(m), dtype=torch.float32, device=a.device) if s is None else s
+    _check(lib().h3x_quant_rows(m, cols, _p(a), _p(q), _p(s), _stream()), "quant_rows")
+    return q, s
+
+
+def norm_mod_quant(cfg, x, shift, scale, q=None, s=None):
+    m, d = x.shape
+    q = torch.zeros(pad_rows(m) * d, dtype=torch.int8, device=x.device) if q is None else q
+    s = torch.zeros(pad_rows(m), dtype=torch.float32, device=x.device) if s is None else s
+    _check(lib().h3x_norm_mod_quant(ctypes.byref(cfg), m, _p(x), _p(shift), _p(scale), _p(q), _p(s), _stream()),
+           "norm_mod_quant")
+    return q, s
+
+
+def linear_a8_f32out(cfg, kind, m, qa, sa, w, sw):
+    out = torch.empty(m, packed_rows(cfg, kind), dtype=torch.float32, device=qa.device)
+    _check(lib().h3x_linear_a8_f32out(ctypes.byref(cfg), kind, m, _p(qa), _p(sa), _p(w), _p(sw), _p(out),
+                                      _stream()), "linear_a8_f32out")
+    return out

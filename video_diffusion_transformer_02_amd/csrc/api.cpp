@@ -83,6 +83,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 int elem_bytes(int act) { return act == H3X_BF16 ? 2 : 4; }
+// Weight types stored as int8 codes with one bfloat16 scale per packed row.
+bool int8_weights(const h3x_block_cfg* c) { return c->weight == H3X_I8 || c->weight == H3X_I8A8; }
 
 // ---------------------------------------------------------------- validation
 h3x_status check_cfg(const h3x_block_cfg* c) {
@@ -94,8 +96,8 @@ h3x_status check_cfg(const h3x_block_cfg* c) {
   if (!(c->norm_eps > 0.f) || !isfinite(c->norm_eps)) return fail(H3X_EINVAL, "cfg: norm_eps must be > 0");
   if (!(c->rope_theta > 1.f) || !isfinite(c->rope_theta)) return fail(H3X_EINVAL, "cfg: rope_theta must be > 1");
   if (c->act != H3X_F32 && c->act != H3X_BF16) return fail(H3X_EINVAL, "cfg: act must be F32 or BF16");
-  if (c->weight != H3X_F32 && c->weight != H3X_BF16 && c->weight != H3X_I8)
-    return fail(H3X_EINVAL, "cfg: weight must be F32, BF16 or I8");
+  if (c->weight != H3X_F32 && c->weight != H3X_BF16 && c->weight != H3X_I8 && c->weight != H3X_I8A8)
+    return fail(H3X_EINVAL, "cfg: weight must be F32, BF16, I8 or I8A8");
   if (c->act == H3X_F32) {
     if (c->weight != H3X_F32) return fail(H3X_ENOTSUP, "cfg: F32 activations need F32 weights");
     if (c->head_dim != 64 && c->head_dim != 128) return fail(H3X_ENOTSUP, "cfg: F32 path supports head_dim 64 or 128");
@@ -105,6 +107,10 @@ h3x_status check_cfg(const h3x_block_cfg* c) {
     if (c->head_dim != 128) return fail(H3X_ENOTSUP, "cfg: BF16 path supports head_dim 128");
     if (c->d_model % 256 || c->ffn_inner % 128)
       return fail(H3X_ENOTSUP, "cfg: BF16 path needs d_model % 256 == 0 and ffn_inner % 128 == 0");
+    // W8A8: the fused norm-quantise kernel holds a row of <= 8192 values in registers, the
+    // quantise kernel one of <= 32768.
+    if (c->weight == H3X_I8A8 && (c->d_model > 8192 || c->ffn_inner > 32768))
+      return fail(H3X_ENOTSUP, "cfg: I8A8 needs d_model <= 8192 and ffn_inner <= 32768");
   }
   return H3X_OK;
 }
@@ -158,6 +164,8 @@ struct BlockWs {
   uint8_t* h;      // [n_pad x F], aliases q, k, vt, o (dead once h is produced)
   uint8_t* rope;   // rope table of the geometry
   uint8_t* attn;   // partial results of key-split attention workgroups
+  uint8_t* a8;     // W8A8: int8 codes of the current projection input, [n_pad x max(d, F)] slabs
+  float* a8s;      // W8A8: their float32 row scales [n_pad]
   size_t bytes;
 };
 
@@ -186,7 +194,14 @@ BlockWs block_layout(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* base) {
   w.q = base + off; w.k = w.q + nd; w.vt = w.k + nd; w.o = w.vt + nd; w.h = w.q;
   off = align256(off + r1);
   w.rope = base + off; off = align256(off + rope_bytes(c, g));
-  w.attn = base + off; off += attn_region_bytes(c, w.n);
+  w.attn = base + off; off = align256(off + attn_region_bytes(c, w.n));
+  w.a8 = nullptr;
+  w.a8s = nullptr;
+  if (c->weight == H3X_I8A8) {
+    const size_t cols = static_cast<size_t>(c->ffn_inner > c->d_model ? c->ffn_inner : c->d_model);
+    w.a8 = base + off; off = align256(off + static_cast<size_t>(w.n_pad) * cols);
+    w.a8s = reinterpret_cast<float*>(base + off); off = align256(off + static_cast<size_t>(w.n_pad) * 4);
+  }
   w.bytes = off;
   return w;
 }
@@ -217,8 +232,8 @@ h3x_status check_weights(const h3x_block_cfg* c, const h3x_block_weights* w) {
   const void* sc[4] = {w->s_qkv, w->s_out, w->s_gate_up, w->s_down};
   for (int i = 0; i < 4; ++i) {
     if (!p[i] || !aligned16(p[i])) return fail(H3X_EINVAL, "weights: NULL or misaligned weight pointer");
-    if (c->weight == H3X_I8 && !sc[i]) return fail(H3X_EINVAL, "weights: int8 weights need scales");
-    if (c->weight != H3X_I8 && sc[i]) return fail(H3X_EINVAL, "weights: scales given for non-int8 weights");
+    if (int8_weights(c) && !sc[i]) return fail(H3X_EINVAL, "weights: int8 weights need scales");
+    if (!int8_weights(c) && sc[i]) return fail(H3X_EINVAL, "weights: scales given for non-int8 weights");
   }
   return H3X_OK;
 }
@@ -239,10 +254,49 @@ GemmArgs gemm_args(const h3x_block_cfg* c, int kind, int64_t m, const void* a, c
   int64_t rows, cols;
   weight_shape(c, kind, &rows, &cols);
   g.a = a; g.w = w; g.wscale = static_cast<const uint16_t*>(s);
+  g.ascale = nullptr;
   g.m = m; g.n = rows; g.k = cols;
   g.m_pad = round_up(m, 256);
   g.d_model = c->d_model;
   return g;
+}
+
+// W8A8 block: every projection input is quantised per row (the normalised rows by the norm
+// kernel itself, the attention output and the SwiGLU product by a pass of their own) into the
+// a8 region, and the GEMMs multiply int8 by int8.
+h3x_status block_forward_a8(const h3x_block_cfg* c, const h3x_geom* g, const h3x_block_weights* w,
+                            const float* mod, void* x, const BlockWs& ws, hipStream_t s) {
+  const int64_t n = ws.n, d = c->d_model;
+  const float *shift1 = mod, *scale1 = mod + d, *gate1 = mod + 2 * d;
+  const float *shift2 = mod + 3 * d, *scale2 = mod + 4 * d, *gate2 = mod + 5 * d;
+  int8_t* qa = reinterpret_cast<int8_t*>(ws.a8);
+  float* sa = ws.a8s;
+  auto args = [&](int kind, const void* wt, const void* sc) {
+    GemmArgs a = gemm_args(c, kind, n, qa, wt, sc);
+    a.ascale = sa;
+    a.a_tiled = 1;
+    return a;
+  };
+  H3X_LAUNCH("norm_mod_quant", s, launch_norm_mod_quant(n, c->d_model, c->norm_eps, x, shift1, scale1, qa, sa, s));
+  GemmArgs qg = args(H3X_W_QKV, w->qkv, w->s_qkv);
+  qg.m_pad = ws.n_pad;
+  qg.q = ws.q; qg.kk = ws.k; qg.vt = ws.vt; qg.geom = geom_dev(*g); qg.rope = rope_dev(c, g, ws.rope);
+  H3X_LAUNCH(gemm_name(EPI_QKV), s, launch_gemm(c->act, c->weight, EPI_QKV, qg, s));
+  H3X_LAUNCH("attention", s, launch_attention(c->act, n, ws.n_pad, c->n_heads, c->head_dim, ws.q, ws.k, ws.vt, ws.o, 0,
+                                              attention_slots(0), ws.attn, s));
+  H3X_LAUNCH("quant_rows", s, launch_quant_rows(n, d, ws.o, qa, sa, s));
+  GemmArgs og = args(H3X_W_OUT, w->out, w->s_out);
+  og.x = x; og.gate = gate1;
+  H3X_LAUNCH("gemm_out_resid", s, launch_gemm(c->act, c->weight, EPI_RESID, og, s));
+  H3X_LAUNCH("norm_mod_quant", s, launch_norm_mod_quant(n, c->d_model, c->norm_eps, x, shift2, scale2, qa, sa, s));
+  GemmArgs gg = args(H3X_W_GATE_UP, w->gate_up, w->s_gate_up);
+  gg.h = ws.h;  // row-major bfloat16, quantised next
+  H3X_LAUNCH(gemm_name(EPI_SWIGLU), s, launch_gemm(c->act, c->weight, EPI_SWIGLU, gg, s));
+  H3X_LAUNCH("quant_rows", s, launch_quant_rows(n, c->ffn_inner, ws.h, qa, sa, s));
+  GemmArgs dg = args(H3X_W_DOWN, w->down, w->s_down);
+  dg.x = x; dg.gate = gate2;
+  H3X_LAUNCH("gemm_down_resid", s, launch_gemm(c->act, c->weight, EPI_RESID, dg, s));
+  return H3X_OK;
 }
 
 // One block on prepared workspace and rope table (no validation).
@@ -253,6 +307,7 @@ h3x_status block_forward_impl(const h3x_block_cfg* c, const h3x_geom* g, const h
   const RopeDev rd = rope_dev(c, g, ws.rope);
   const float *shift1 = mod, *scale1 = mod + d, *gate1 = mod + 2 * d;
   const float *shift2 = mod + 3 * d, *scale2 = mod + 4 * d, *gate2 = mod + 5 * d;
+  if (c->weight == H3X_I8A8) return block_forward_a8(c, g, w, mod, x, ws, s);
 
   // bf16: the GEMM A operands (y, o, y2, h) live in the slab layout of the MFMA GEMM.
   const int tiled = c->act == H3X_BF16 ? 1 : 0;
@@ -349,7 +404,7 @@ size_t h3x_packed_weight_bytes(const h3x_block_cfg* c, int32_t kind) {
   int64_t r, cc;
   weight_shape(c, kind, &r, &cc);
   if (r < 0) return 0;
-  const size_t es = c->weight == H3X_I8 ? 1 : (c->weight == H3X_BF16 ? 2 : 4);
+  const size_t es = int8_weights(c) ? 1 : (c->weight == H3X_BF16 ? 2 : 4);
   return static_cast<size_t>(r) * cc * es;
 }
 
@@ -358,14 +413,14 @@ int64_t h3x_packed_scale_count(const h3x_block_cfg* c, int32_t kind) {
   int64_t r, cc;
   weight_shape(c, kind, &r, &cc);
   if (r < 0) return -1;
-  return c->weight == H3X_I8 ? r : 0;
+  return int8_weights(c) ? r : 0;
 }
 
 h3x_status h3x_pack_weights(const h3x_block_cfg* c, int32_t kind, const void* w, void* packed,
                             void* stream) {
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
-  if (c->weight == H3X_I8) return fail(H3X_EINVAL, "pack_weights: use h3x_pack_int8_weights for I8 configs");
+  if (int8_weights(c)) return fail(H3X_EINVAL, "pack_weights: use h3x_pack_int8_weights for I8 / I8A8 configs");
   int64_t rows, cols;
   weight_shape(c, kind, &rows, &cols);
   if (rows < 0) return fail(H3X_EINVAL, "pack_weights: bad kind");
@@ -380,7 +435,7 @@ h3x_status h3x_pack_int8_weights(const h3x_block_cfg* c, int32_t kind, const voi
                                  void* q_packed, void* scale_bf16, void* stream) {
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
-  if (c->weight != H3X_I8) return fail(H3X_EINVAL, "pack_int8_weights: cfg->weight must be I8");
+  if (!int8_weights(c)) return fail(H3X_EINVAL, "pack_int8_weights: cfg->weight must be I8 or I8A8");
   int64_t rows, cols;
   weight_shape(c, kind, &rows, &cols);
   if (rows < 0) return fail(H3X_EINVAL, "pack_int8_weights: bad kind");
@@ -388,7 +443,7 @@ h3x_status h3x_pack_int8_weights(const h3x_block_cfg* c, int32_t kind, const voi
     return fail(H3X_EINVAL, "pack_int8_weights: NULL or misaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
   H3X_LAUNCH("pack_int8", s, launch_pack_int8(kind, rows, cols, w_bf16, static_cast<int8_t*>(q_packed),
-                                              static_cast<uint16_t*>(scale_bf16), s));
+                                              static_cast<uint16_t*>(scale_bf16), c->weight == H3X_I8A8, s));
   return H3X_OK;
 }
 
@@ -545,12 +600,14 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
     bw.n_pad = round_up(bw.n, 256);
     // Re-derive the y and R1 arenas for the (smaller) merged sequence inside the unmerged ones.
     // Only those two are re-laid: past them lies the unmerged rope table, which the blocks after
-    // the reduced range still read, so the merged rope table and the attention pieces keep
-    // regions of their own (the unmerged attention region bounds the merged one).
+    // the reduced range still read, so the merged rope table, the attention pieces and the W8A8
+    // codes keep regions of their own (each unmerged region bounds the merged one).
     if (merged) {
       BlockWs m = block_layout(c, gb, lay.blk.y);
       m.rope = lay.rope_m;
       m.attn = lay.blk.attn;
+      m.a8 = lay.blk.a8;
+      m.a8s = lay.blk.a8s;
       bw = m;
     }
     if ((st = block_forward_impl(c, gb, &st_->blocks[b], st_->mod + b * mod_stride,
@@ -601,6 +658,7 @@ h3x_status h3x_qkv_project(const h3x_block_cfg* c, const h3x_geom* g, const void
   if (!y || !w_qkv || !rope_table || !q || !k || !vt) return fail(H3X_EINVAL, "qkv_project: NULL pointer");
   if (!aligned16(y) || !aligned16(w_qkv) || !aligned16(rope_table) || !aligned16(q) || !aligned16(k) || !aligned16(vt))
     return fail(H3X_EINVAL, "qkv_project: misaligned pointer");
+  if (c->weight == H3X_I8A8) return fail(H3X_ENOTSUP, "qkv_project: I8A8 projections run inside the block");
   if ((c->weight == H3X_I8) != (s_qkv != nullptr)) return fail(H3X_EINVAL, "qkv_project: scales iff int8 weights");
   const int64_t n = geom_tokens(g);
   GemmArgs a = gemm_args(c, H3X_W_QKV, n, y, w_qkv, s_qkv);
@@ -641,7 +699,51 @@ static h3x_status linear_common(const h3x_block_cfg* c, int32_t kind, int64_t m,
   if (kind < H3X_W_QKV || kind > H3X_W_DOWN) return fail(H3X_EINVAL, "linear: bad kind");
   if (m < 0 || m > (int64_t(1) << 26)) return fail(H3X_EINVAL, "linear: bad m");
   if (!a || !w || !aligned16(a) || !aligned16(w)) return fail(H3X_EINVAL, "linear: NULL or misaligned pointer");
+  if (c->weight == H3X_I8A8) return fail(H3X_ENOTSUP, "linear: I8A8 takes quantised activations (h3x_linear_a8_f32out)");
   if ((c->weight == H3X_I8) != (sc != nullptr)) return fail(H3X_EINVAL, "linear: scales iff int8 weights");
+  return H3X_OK;
+}
+
+h3x_status h3x_quant_rows(int64_t m, int64_t cols, const void* a, void* q, float* sc, void* stream) {
+  if (m < 0 || m > (int64_t(1) << 26)) return fail(H3X_EINVAL, "quant_rows: bad m");
+  if (cols <= 0 || cols % 64 || cols > 32768) return fail(H3X_EINVAL, "quant_rows: need 0 < cols <= 32768, cols % 64 == 0");
+  if (!a || !q || !sc || !aligned16(a) || !aligned16(q) || !aligned16(sc))
+    return fail(H3X_EINVAL, "quant_rows: NULL or misaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("quant_rows", s, launch_quant_rows(m, cols, a, static_cast<int8_t*>(q), sc, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_norm_mod_quant(const h3x_block_cfg* c, int64_t n_rows, const void* x, const float* shift,
+                              const float* scale, void* q, float* sc, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if (c->weight != H3X_I8A8) return fail(H3X_EINVAL, "norm_mod_quant: cfg->weight must be I8A8");
+  if (n_rows < 0 || n_rows > (int64_t(1) << 26)) return fail(H3X_EINVAL, "norm_mod_quant: bad n_rows");
+  if (!x || !shift || !scale || !q || !sc || !aligned16(x) || !aligned16(shift) || !aligned16(scale) ||
+      !aligned16(q) || !aligned16(sc))
+    return fail(H3X_EINVAL, "norm_mod_quant: NULL or misaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH("norm_mod_quant", s, launch_norm_mod_quant(n_rows, c->d_model, c->norm_eps, x, shift, scale,
+                                                        static_cast<int8_t*>(q), sc, s));
+  return H3X_OK;
+}
+
+h3x_status h3x_linear_a8_f32out(const h3x_block_cfg* c, int32_t kind, int64_t m, const void* qa, const float* sa,
+                                const void* w, const void* sw, float* out, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if (c->weight != H3X_I8A8) return fail(H3X_EINVAL, "linear_a8_f32out: cfg->weight must be I8A8");
+  if (kind < H3X_W_QKV || kind > H3X_W_DOWN) return fail(H3X_EINVAL, "linear_a8_f32out: bad kind");
+  if (m < 0 || m > (int64_t(1) << 26)) return fail(H3X_EINVAL, "linear_a8_f32out: bad m");
+  if (!qa || !sa || !w || !sw || !out || !aligned16(qa) || !aligned16(sa) || !aligned16(w) || !aligned16(out))
+    return fail(H3X_EINVAL, "linear_a8_f32out: NULL or misaligned pointer");
+  GemmArgs g = gemm_args(c, kind, m, qa, w, sw);
+  g.ascale = sa;
+  g.a_tiled = 1;
+  g.out = out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  H3X_LAUNCH(gemm_name(EPI_F32), s, launch_gemm(c->act, c->weight, EPI_F32, g, s));
   return H3X_OK;
 }
 

@@ -15,6 +15,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Plain 16- and 8-byte vectors (ext_vector types stay in registers, unlike HIP's uint4 struct).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- element conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

@@ -1,6 +1,8 @@
-// Memory-bound kernels of the hot path: modulated RMSNorm, token merge / unmerge, the Euler
-// update, assembly of the DiT input, weight packing (bf16 / f32 permutation and int8
-// quantisation), the 3D RoPE table and a plain copy. All move 16 bytes per lane per access.
+// Memory-bound kernels of the hot path: modulated RMSNorm (optionally fused with the per-row
+// int8 quantisation of its output), per-row int8 quantisation of activations, token merge /
+// unmerge, the Euler update, assembly of the DiT input, weight packing (bf16 / f32 permutation
+// and int8 quantisation), the 3D RoPE table and a plain copy. All read 16 bytes per lane per
+// access.
 #include <math.h>
 
 #include "launch.h"
@@ -162,6 +164,171 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(const typename E::T
       else
         store16<E>(y + row * d + i, o);
     }
+  }
+}
+
+// ---------------------------------------------------------------- per-row int8 activations
+// Quantisation parameters of a row whose largest magnitude is a: inv = 127 / a and s = a / 127
+// (IEEE float32 divisions); a == 0 or an inverse that overflows gives s = 0 and zero codes.
+__device__ __forceinline__ void quant_params(float a, float& inv, float& s) {
+  inv = 127.0f / a;
+  s = a / 127.0f;
+  if (!(inv <= 3.402823466e38f)) {  // a == 0, or a so small that 127 / a is infinite
+    inv = 0.f;
+    s = 0.f;
+  }
+}
+// Eight values -> eight codes clamp(rint(v * inv), -127, 127) packed little-endian.
+__device__ __forceinline__ uint2 quant8(const float* v, float inv) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int qi = static_cast<int>(fminf(fmaxf(rintf(v[j] * inv), -127.f), 127.f));
+    const uint32_t b = static_cast<uint32_t>(qi) & 0xffu;
+    if (j < 4) lo |= b << (8 * j); else hi |= b << (8 * (j - 4));
+  }
+  return make_uint2(lo, hi);
+}
+
+// Largest value over the workgroup for each of kRows rows (part: kRows x 4 floats of LDS).
+template <int kRows>
+__device__ __forceinline__ void block_max_rows(float* m, float (*part)[kThreads / 64]) {
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    m[r] = wave_max(m[r]);
+    if ((threadIdx.x & 63) == 0) part[r][threadIdx.x >> 6] = m[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    float a = part[r][0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) a = fmaxf(a, part[r][w]);
+    m[r] = a;
+  }
+}
+
+// Modulated RMSNorm of kRows bfloat16 rows (the arithmetic of norm_rows_kernel), rounded to
+// bfloat16, then quantised per row: codes in slab_offset_q8 order, float32 scales.
+template <int kChunks, int kRows>
+__global__ __launch_bounds__(kThreads) void norm_quant_kernel(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ shift,
+                                                              const float* __restrict__ scale,
+                                                              int8_t* __restrict__ q,
+                                                              float* __restrict__ qscale,
+                                                              int64_t n_rows, int d, float eps) {
+  constexpr int V = 8;
+  __shared__ float part[kRows][kThreads / 64];
+  __shared__ float pmax[kRows][kThreads / 64];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  float v[kRows][kChunks][V];
+  float ss[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    ss[r] = 0.f;
+    const int64_t row = r0 + r;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int i = (c * kThreads + threadIdx.x) * V;
+      if (row < n_rows && i < d) {
+        load16<BF16>(x + row * d + i, v[r][c]);
+#pragma unroll
+        for (int j = 0; j < V; ++j) ss[r] = fmaf(v[r][c][j], v[r][c][j], ss[r]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) v[r][c][j] = 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    ss[r] = wave_sum(ss[r]);
+    if ((threadIdx.x & 63) == 0) part[r][threadIdx.x >> 6] = ss[r];
+  }
+  __syncthreads();
+  float rs[kRows], amax[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) tot += part[r][w];
+    rs[r] = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
+    amax[r] = 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int i = (c * kThreads + threadIdx.x) * V;
+    if (i >= d) continue;
+    float sc[V], sh[V];
+#pragma unroll
+    for (int j = 0; j < V / 4; ++j) {
+      const float4 a = reinterpret_cast<const float4*>(scale + i)[j];
+      const float4 b = reinterpret_cast<const float4*>(shift + i)[j];
+      sc[4 * j] = 1.f + a.x; sc[4 * j + 1] = 1.f + a.y; sc[4 * j + 2] = 1.f + a.z; sc[4 * j + 3] = 1.f + a.w;
+      sh[4 * j] = b.x; sh[4 * j + 1] = b.y; sh[4 * j + 2] = b.z; sh[4 * j + 3] = b.w;
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const float o = bf16_bits_to_f32(f32_to_bf16_bits(fmaf(v[r][c][j] * rs[r], sc[j], sh[j])));
+        v[r][c][j] = o;
+        amax[r] = fmaxf(amax[r], fabsf(o));
+      }
+  }
+  block_max_rows<kRows>(amax, pmax);
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int64_t row = r0 + r;
+    if (row >= n_rows) continue;
+    float inv, s;
+    quant_params(amax[r], inv, s);
+    if (threadIdx.x == 0) qscale[row] = s;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int i = (c * kThreads + threadIdx.x) * V;
+      if (i < d) *reinterpret_cast<uint2*>(q + slab_offset_q8(row, i, d)) = quant8(v[r][c], inv);
+    }
+  }
+}
+
+// One workgroup per bfloat16 row [cols]: the row stays in registers (kChunks 16-byte chunks per
+// thread, cols <= kChunks * 2048), amax over the workgroup, then codes and scale as above.
+template <int kChunks>
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(const uint16_t* __restrict__ a,
+                                                              int8_t* __restrict__ q,
+                                                              float* __restrict__ qscale,
+                                                              int64_t cols) {
+  __shared__ float pmax[1][kThreads / 64];
+  const int64_t row = blockIdx.x;
+  const uint16_t* ar = a + row * cols;
+  u32x4 raw[kChunks];
+  float amax[1] = {0.f};
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int64_t i = (c * kThreads + threadIdx.x) * 8;
+    raw[c] = u32x4{0u, 0u, 0u, 0u};
+    if (i < cols) raw[c] = *reinterpret_cast<const u32x4*>(ar + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      amax[0] = fmaxf(amax[0], fmaxf(fabsf(__uint_as_float(raw[c][j] << 16)),
+                                     fabsf(__uint_as_float(raw[c][j] & 0xffff0000u))));
+  }
+  block_max_rows<1>(amax, pmax);
+  float inv, s;
+  quant_params(amax[0], inv, s);
+  if (threadIdx.x == 0) qscale[row] = s;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int64_t i = (c * kThreads + threadIdx.x) * 8;
+    if (i >= cols) continue;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(raw[c][j] << 16);
+      v[2 * j + 1] = __uint_as_float(raw[c][j] & 0xffff0000u);
+    }
+    *reinterpret_cast<uint2*>(q + slab_offset_q8(row, i, cols)) = quant8(v, inv);
   }
 }
 
@@ -391,12 +558,13 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const T* __restrict__ w,
 }
 
 // One workgroup per packed row: amax, scale = bf16(amax / 127), codes = clamp(rint(w / s)).
-// Codes are stored as 256-row x 32-byte slabs (slab_offset_i8); scales in packed row order.
+// Codes are stored as 256-row x 32-byte slabs (slab_offset_i8), or as 256-row x 64-byte slabs
+// (slab_offset_q8) for the W8A8 GEMM; scales in packed row order.
 __global__ __launch_bounds__(kThreads) void pack_int8_kernel(const uint16_t* __restrict__ w,
                                                              int8_t* __restrict__ q,
                                                              uint16_t* __restrict__ scale,
                                                              int kind, int64_t rows,
-                                                             int64_t cols) {
+                                                             int64_t cols, int slab64) {
   __shared__ float part[kThreads / 64];
   const int64_t p = blockIdx.x;
   const int64_t src = packed_source_row(kind, p, rows);
@@ -428,7 +596,8 @@ __global__ __launch_bounds__(kThreads) void pack_int8_kernel(const uint16_t* __r
       const uint32_t b = static_cast<uint32_t>(qi) & 0xffu;
       if (j < 4) lo |= b << (8 * j); else hi |= b << (8 * (j - 4));
     }
-    *reinterpret_cast<uint2*>(q + slab_offset_i8(p, c, cols)) = make_uint2(lo, hi);
+    const int64_t off = slab64 ? slab_offset_q8(p, c, cols) : slab_offset_i8(p, c, cols);
+    *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
   }
 }
 
@@ -580,9 +749,43 @@ hipError_t launch_pack(int wdtype, int kind, int64_t rows, int64_t cols, const v
 }
 
 hipError_t launch_pack_int8(int kind, int64_t rows, int64_t cols, const void* w_bf16,
-                            int8_t* q, uint16_t* scale, hipStream_t s) {
+                            int8_t* q, uint16_t* scale, int slab64, hipStream_t s) {
   pack_int8_kernel<<<dim3(rows), kThreads, 0, s>>>(static_cast<const uint16_t*>(w_bf16), q,
-                                                  scale, kind, rows, cols);
+                                                  scale, kind, rows, cols, slab64);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(int64_t n_rows, int64_t cols, const void* a, int8_t* q, float* qscale,
+                             hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  if (cols % 64 || cols > 16 * kThreads * 8) return hipErrorInvalidValue;
+  const uint16_t* aa = static_cast<const uint16_t*>(a);
+  const dim3 grid(static_cast<unsigned>(n_rows));
+  const int64_t chunks = (cols + kThreads * 8 - 1) / (kThreads * 8);
+  if (chunks <= 1) quant_rows_kernel<1><<<grid, kThreads, 0, s>>>(aa, q, qscale, cols);
+  else if (chunks <= 2) quant_rows_kernel<2><<<grid, kThreads, 0, s>>>(aa, q, qscale, cols);
+  else if (chunks <= 3) quant_rows_kernel<3><<<grid, kThreads, 0, s>>>(aa, q, qscale, cols);
+  else if (chunks <= 4) quant_rows_kernel<4><<<grid, kThreads, 0, s>>>(aa, q, qscale, cols);
+  else if (chunks <= 6) quant_rows_kernel<6><<<grid, kThreads, 0, s>>>(aa, q, qscale, cols);
+  else if (chunks <= 8) quant_rows_kernel<8><<<grid, kThreads, 0, s>>>(aa, q, qscale, cols);
+  else if (chunks <= 12) quant_rows_kernel<12><<<grid, kThreads, 0, s>>>(aa, q, qscale, cols);
+  else quant_rows_kernel<16><<<grid, kThreads, 0, s>>>(aa, q, qscale, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_mod_quant(int64_t n_rows, int d, float eps, const void* x, const float* shift,
+                                 const float* scale, int8_t* q, float* qscale, hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  if (d % 64 || d > 4 * kThreads * 8) return hipErrorInvalidValue;
+  constexpr int kRows = 4;
+  const unsigned grid = static_cast<unsigned>((n_rows + kRows - 1) / kRows);
+  const uint16_t* xx = static_cast<const uint16_t*>(x);
+  switch ((d + kThreads * 8 - 1) / (kThreads * 8)) {
+    case 1: norm_quant_kernel<1, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, q, qscale, n_rows, d, eps); break;
+    case 2: norm_quant_kernel<2, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, q, qscale, n_rows, d, eps); break;
+    case 3: norm_quant_kernel<3, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, q, qscale, n_rows, d, eps); break;
+    default: norm_quant_kernel<4, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, q, qscale, n_rows, d, eps); break;
+  }
   return hipGetLastError();
 }
 

@@ -8,7 +8,11 @@
 //    each per SIMD) run ping-pong: while one issues its MFMAs the other reads its next
 //    fragments and streams the next K step, offset by one barrier interval. int8 weights are
 //    widened to bfloat16 in registers (exact: |q| <= 127) and their per-row scale is applied in
-//    the epilogue. Workgroups are remapped so that each XCD (own L2) walks a contiguous run of
+//    the epilogue. W8A8 (int8 weights and per-row int8 activations): the same pipeline over
+//    64-code K steps (a 256 x 64-byte slab per operand, the byte layout of a bfloat16 step) on
+//    v_mfma_i32_32x32x32_i8 with int32 accumulation; the epilogue converts the exact integer
+//    sums to float32 and applies the activation row scale and the weight column scale.
+//    Workgroups are remapped so that each XCD (own L2) walks a contiguous run of
 //    a grouped tile order: consecutive tiles share weight panels and activation panels.
 //  * gemm_f32_kernel: float32 activations and weights (small configurations): 64 x 64 tiles,
 //    plain FMA, same epilogues.
@@ -18,6 +22,8 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <type_traits>
 
 #include "launch.h"
 
@@ -112,9 +118,10 @@ struct Layout {
   static constexpr int NB = SN / 32;   // 32-wide MFMA blocks per wave along N
 };
 
-template <bool kInt8, int kEpi, int kWN, bool kATiled, bool kPingPong = false>
+template <bool kInt8, int kEpi, int kWN, bool kATiled, bool kPingPong, bool kA8>
 __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(GemmArgs p, int tiles_m,
                                                                                 int tiles_n, int group_m) {
+  static_assert(!kA8 || (kATiled && !kInt8), "W8A8 takes tiled int8 activations and 64-byte weight slabs");
   using L = Layout<kWN>;
   constexpr int NB = L::NB, SN = L::SN, kWaves = L::kWaves;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<kInt8>::kTotal];
@@ -138,7 +145,8 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   const int wm = wave / kWN, wn = wave % kWN;
   const int li = lane & 31, hi = lane >> 5;
   const int64_t K = p.k;
-  const int ktiles = static_cast<int>(K / BK);
+  constexpr int kKStep = kA8 ? 64 : BK;  // K elements per pipeline step: 64 bytes of a row
+  const int ktiles = static_cast<int>(K / kKStep);
 
   // ---- global -> LDS without registers: buffer_load_dwordx4 ... lds writes lane l's 16 bytes
   // at (wave-uniform base) + 16 l, so one wave instruction fills 1 KB of a stage.
@@ -149,13 +157,13 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   //    swizzle places at its LDS position; rows past the end of A lie outside the buffer's range
   //    and read as zeros.
   constexpr int kSlabA = BM * BK * 2, kSlabB = BN * BK * (kInt8 ? 1 : 2);
-  const uint8_t* Ab = static_cast<const uint8_t*>(p.a) + (kATiled ? tm * (K / BK) * kSlabA : m0 * K * 2);
-  const uint8_t* Wb = static_cast<const uint8_t*>(p.w) + tn * (K / BK) * kSlabB;
+  const uint8_t* Ab = static_cast<const uint8_t*>(p.a) + (kATiled ? tm * (K / kKStep) * kSlabA : m0 * K * 2);
+  const uint8_t* Wb = static_cast<const uint8_t*>(p.w) + tn * (K / kKStep) * kSlabB;
   const int64_t a_rows = p.m - m0 < BM ? p.m - m0 : BM;
   const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(Ab), 0, static_cast<int>(kATiled ? (K / BK) * kSlabA : a_rows * K * 2), 0x00020000);
+      const_cast<uint8_t*>(Ab), 0, static_cast<int>(kATiled ? (K / kKStep) * kSlabA : a_rows * K * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(Wb), 0, static_cast<int>((K / BK) * kSlabB), 0x00020000);
+      const_cast<uint8_t*>(Wb), 0, static_cast<int>((K / kKStep) * kSlabB), 0x00020000);
   const uint32_t lin_voff = static_cast<uint32_t>(wave * 1024 + lane * 16);
   const uint32_t lin_step = static_cast<uint32_t>(kWaves * 1024);
   const int a_row = lane >> 2, a_chunk = (lane & 3) ^ ((lane >> 4) & 3);
@@ -182,26 +190,28 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
                                                b_voff + i * b_step, kb, 0, 0);
   };
 
-  f32x16 acc[4][NB];
+  using Acc = std::conditional_t<kA8, i32x16, f32x16>;
+  Acc acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  // Operand fragments of one 16-wide K slice: A rows of the four m-blocks, B rows of the
-  // n-blocks (int8 weights stay packed until just before the multiply).
+  // Operand fragments of one K slice (16 bfloat16 values, or 32 codes for W8A8: 32 bytes of a
+  // row either way): A rows of the four m-blocks, B rows of the n-blocks (int8 weights of the
+  // bfloat16 path stay packed until just before the multiply).
   struct Frags {
-    bf16x8 a[4];
-    u32x4 b[NB];  // bf16: 8 values; int8: 8 codes in .xy
+    u32x4 a[4];   // bf16: 8 values; W8A8: 16 codes
+    u32x4 b[NB];  // bf16: 8 values; int8: 8 codes in .xy; W8A8: 16 codes
   };
   auto read_frags = [&](int kt, int slice, Frags& f) {
     const uint8_t* sa = smem + (kt % kStages) * Smem<kInt8>::kStage;
     const uint8_t* sb = sa + Smem<kInt8>::kA;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      f.a[mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + swz16(wm * 128 + mb * 32 + li, 2 * slice + hi)));
+      f.a[mb] = *reinterpret_cast<const u32x4*>(sa + swz16(wm * 128 + mb * 32 + li, 2 * slice + hi));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int row = wn * SN + nb * 32 + li;
@@ -214,6 +224,15 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
     }
   };
   auto mma = [&](const Frags& f) {
+    if constexpr (kA8) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, f.a[mb]),
+                                                             __builtin_bit_cast(i32x4, f.b[nb]), acc[mb][nb], 0, 0, 0);
+      return;
+    }
     bf16x8 bv[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -224,7 +243,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a[mb]), bv[nb], acc[mb][nb], 0, 0, 0);
   };
   // One LDS read between consecutive MFMAs until the next slice's fragments are all requested,
   // then the remaining MFMAs back to back; kVmem buffer loads ride along with each pair.
@@ -333,7 +352,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   float csc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) csc[j] = 1.0f;
-  if constexpr (kInt8 && kEpi != EPI_SWIGLU) {
+  if constexpr ((kInt8 || kA8) && kEpi != EPI_SWIGLU) {
     const u32x4 sraw = *reinterpret_cast<const u32x4*>(p.wscale + col_base + lc);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -349,7 +368,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        st[(8 * (e >> 2) + 4 * hi + (e & 3)) * kStride + nb * 32 + li] = acc[mb][nb][e];
+        st[(8 * (e >> 2) + 4 * hi + (e & 3)) * kStride + nb * 32 + li] = static_cast<float>(acc[mb][nb][e]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t r0 = row_base + mb * 32;
 
@@ -361,6 +380,11 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc + 4);
         float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        if constexpr (kA8) {
+          const float rs = p.ascale[row];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] *= rs;
+        }
         if (row < p.m) {
           if constexpr (kEpi == EPI_F32) {
             float* o = p.out + row * p.n + col_base + lc;
@@ -394,7 +418,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
       float sg[8], su[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) { sg[j] = 1.0f; su[j] = 1.0f; }
-      if constexpr (kInt8) {
+      if constexpr (kInt8 || kA8) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(p.wscale + col_base + gcol);
         const u32x4 b = *reinterpret_cast<const u32x4*>(p.wscale + col_base + ucol);
 #pragma unroll
@@ -413,8 +437,13 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
         const f32x4 gb = *reinterpret_cast<const f32x4*>(st + r * kStride + gcol + 4);
         const f32x4 ua = *reinterpret_cast<const f32x4*>(st + r * kStride + ucol);
         const f32x4 ub = *reinterpret_cast<const f32x4*>(st + r * kStride + ucol + 4);
-        const float gv[8] = {ga[0], ga[1], ga[2], ga[3], gb[0], gb[1], gb[2], gb[3]};
-        const float uv[8] = {ua[0], ua[1], ua[2], ua[3], ub[0], ub[1], ub[2], ub[3]};
+        float gv[8] = {ga[0], ga[1], ga[2], ga[3], gb[0], gb[1], gb[2], gb[3]};
+        float uv[8] = {ua[0], ua[1], ua[2], ua[3], ub[0], ub[1], ub[2], ub[3]};
+        if constexpr (kA8) {
+          const float rs = p.ascale[row];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) { gv[j] *= rs; uv[j] *= rs; }
+        }
         if (row < p.m) {
           u32x4 out;
 #pragma unroll
@@ -448,6 +477,11 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
           const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc + 4);
           float v[8] = {v0[0] * csc[0], v0[1] * csc[1], v0[2] * csc[2], v0[3] * csc[3],
                         v1[0] * csc[4], v1[1] * csc[5], v1[2] * csc[6], v1[3] * csc[7]};
+          if constexpr (kA8) {
+            const float rs = p.ascale[row];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] *= rs;
+          }
           if (row < p.geom.n_video) {
             const int4 rb = p.rope.rowbase[row];
             const int base = (axis == 0 ? rb.x : (axis == 1 ? rb.y : rb.z)) + k0;
@@ -482,15 +516,20 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
           const int c = lane + 64 * half;
           const int64_t f = col_base + c - 2 * d;
           float sc = 1.0f;
-          if constexpr (kInt8) sc = bf16_bits_to_f32(p.wscale[col_base + c]);
+          if constexpr (kInt8 || kA8) sc = bf16_bits_to_f32(p.wscale[col_base + c]);
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             u32x4 out;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int r = q4 * 8 + 2 * j;
-              const float y0 = r0 + r < p.m ? st[r * kStride + c] * sc : 0.f;
-              const float y1 = r0 + r + 1 < p.m ? st[(r + 1) * kStride + c] * sc : 0.f;
+              float s0 = sc, s1 = sc;
+              if constexpr (kA8) {
+                s0 *= p.ascale[r0 + r];
+                s1 *= p.ascale[r0 + r + 1];
+              }
+              const float y0 = r0 + r < p.m ? st[r * kStride + c] * s0 : 0.f;
+              const float y1 = r0 + r + 1 < p.m ? st[(r + 1) * kStride + c] * s1 : 0.f;
               out[j] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
                        (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
             }
@@ -585,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
   }
 }
 
-template <bool kInt8, int kWN, bool kATiled, bool kPP>
+template <bool kInt8, int kWN, bool kATiled, bool kPP, bool kA8 = false>
 hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   const int tiles_m = static_cast<int>((a.m + BM - 1) / BM);
   const int tiles_n = static_cast<int>(a.n / BN);
@@ -595,16 +634,16 @@ hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   constexpr int T = Layout<kWN>::kThreadsT;
   switch (epi) {
     case EPI_QKV:
-      gemm_mfma_kernel<kInt8, EPI_QKV, kWN, kATiled, kPP><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_QKV, kWN, kATiled, kPP, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_RESID:
-      gemm_mfma_kernel<kInt8, EPI_RESID, kWN, kATiled, kPP><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_RESID, kWN, kATiled, kPP, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_SWIGLU:
-      gemm_mfma_kernel<kInt8, EPI_SWIGLU, kWN, kATiled, kPP><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_SWIGLU, kWN, kATiled, kPP, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     default:
-      gemm_mfma_kernel<kInt8, EPI_F32, kWN, kATiled, kPP><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_F32, kWN, kATiled, kPP, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
   }
   return hipGetLastError();
@@ -641,6 +680,10 @@ hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& a, hipStrea
       default: gemm_f32_kernel<EPI_F32><<<grid, kThreads, 0, s>>>(a); break;
     }
     return hipGetLastError();
+  }
+  if (wdtype == H3X_I8A8) {
+    if (gemm_mode_pp()) return launch_mfma<false, 4, true, true, true>(epi, a, s);
+    return launch_mfma<false, 4, true, false, true>(epi, a, s);
   }
   const bool i8 = wdtype == H3X_I8;
   if (a.a_tiled) return i8 ? launch_mode<true, true>(epi, a, s) : launch_mode<false, true>(epi, a, s);

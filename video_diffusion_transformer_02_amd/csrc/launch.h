@@ -28,8 +28,18 @@ hipError_t launch_rope_table(const GeomDev& g, int head_dim, float theta, float2
                              int4* rowbase, hipStream_t s);
 hipError_t launch_pack(int wdtype, int kind, int64_t rows, int64_t cols, const void* w,
                        void* packed, hipStream_t s);
+// slab64 = 0: codes in slab_offset_i8 order (int8 weights, bfloat16 activations); 1: in
+// slab_offset_q8 order (int8 weights and int8 activations).
 hipError_t launch_pack_int8(int kind, int64_t rows, int64_t cols, const void* w_bf16,
-                            int8_t* q, uint16_t* scale, hipStream_t s);
+                            int8_t* q, uint16_t* scale, int slab64, hipStream_t s);
+// Per-row int8 quantisation of bfloat16 rows (row-major [n_rows x cols]): codes q in
+// slab_offset_q8 order, float32 scales qscale[n_rows]. cols % 64 == 0, cols <= 32768.
+hipError_t launch_quant_rows(int64_t n_rows, int64_t cols, const void* a, int8_t* q, float* qscale,
+                             hipStream_t s);
+// Modulated RMSNorm (bfloat16) followed by the per-row quantisation of its bfloat16-rounded
+// output: codes and scales as launch_quant_rows. d <= 8192.
+hipError_t launch_norm_mod_quant(int64_t n_rows, int d, float eps, const void* x, const float* shift,
+                                 const float* scale, int8_t* q, float* qscale, hipStream_t s);
 
 // Byte offset of bf16 element (r, c) of a [rows x k] matrix stored as 256-row x 32-column slabs:
 // slab (r / 256, c / 32) at ((r / 256) * (k / 32) + c / 32) * 16 KB; inside it, row rr = r % 256
@@ -46,6 +56,15 @@ __host__ __device__ inline int64_t slab_offset(int64_t r, int64_t c, int64_t k) 
 __host__ __device__ inline int64_t slab_offset_i8(int64_t r, int64_t c, int64_t k) {
   const int64_t rr = r & 255, cc = c & 31;
   return (((r >> 8) * (k >> 5) + (c >> 5)) << 13) + rr * 32 + ((((cc >> 4) ^ ((rr >> 3) & 1))) << 4) +
+         (cc & 15);
+}
+
+// Same for int8 codes of the W8A8 GEMM: 256 x 64-byte slabs of 16 KB, the byte layout of the
+// bfloat16 slabs (four 16-byte chunks per row permuted by chunk ^ ((rr >> 2) & 3)), so that one
+// K step covers 64 codes. k must be a multiple of 64.
+__host__ __device__ inline int64_t slab_offset_q8(int64_t r, int64_t c, int64_t k) {
+  const int64_t rr = r & 255, cc = c & 63;
+  return (((r >> 8) * (k >> 6) + (c >> 6)) << 14) + rr * 64 + ((((cc >> 4) ^ ((rr >> 2) & 3))) << 4) +
          (cc & 15);
 }
 
@@ -66,8 +85,10 @@ enum Epi : int {
 };
 
 struct GemmArgs {
-  const void* a;        // [m x k] act type: row-major, or slabs (a_tiled) as slab_offset()
-  int a_tiled;          // bf16 MFMA path only
+  const void* a;        // [m x k] act type: row-major, or slabs (a_tiled) as slab_offset();
+                        // int8 codes as slab_offset_q8() for W8A8 weights
+  const float* ascale;  // W8A8: float32 scale per row of a (m rounded up to 256 entries)
+  int a_tiled;          // bf16 MFMA path only (always set for W8A8)
   int out_tiled;        // EPI_SWIGLU: h written as slabs instead of row-major
   const void* w;        // packed weight [n x k] (bf16, f32 or int8 codes)
   const uint16_t* wscale;  // int8 scales [n] (bfloat16) or nullptr
