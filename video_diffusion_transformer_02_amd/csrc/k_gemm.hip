@@ -39,6 +39,10 @@ constexpr int kStages = H3X_GEMM_STAGES;  // LDS stages of the K pipeline (32 KB
 
 // ---------------------------------------------------------------- shared epilogue math
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// The same with the hardware reciprocal (1 ulp) in place of the IEEE division: the bfloat16 h
+// it feeds rounds far more coarsely, and the division's refinement steps were a visible part of
+// the SwiGLU epilogue.
+__device__ __forceinline__ float silu_rcp(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // Table index of the (cos, sin) entry turning pair `dh/2` of video row `row`.
 __device__ __forceinline__ int rope_index(const RopeDev& r, int64_t row, int dh) {
@@ -360,9 +364,100 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
       csc[2 * j + 1] = __uint_as_float(sraw[j] & 0xffff0000u);
     }
   }
+  // Global operands of the row-wise epilogues are fetched one 32-row slice ahead, so that their
+  // latency is paid once per tile rather than once per slice: the residual rows of x and the
+  // activation row scales (W8A8). The gated residual's column factors gate * scale are formed
+  // once.
+  constexpr int kIt = 32 / kRowsPass;
+  [[maybe_unused]] u32x4 xbuf[2][kIt];
+  [[maybe_unused]] float rbuf[2][kIt];
+  [[maybe_unused]] float gsc[8];
+  auto fetch_rows = [&](int mb) {
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int64_t row = row_base + mb * 32 + it * kRowsPass + lr;
+      if constexpr (kEpi == EPI_RESID) {
+        xbuf[mb & 1][it] = u32x4{0u, 0u, 0u, 0u};
+        if (row < p.m)
+          xbuf[mb & 1][it] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.x) + row * p.n + col_base + lc);
+      }
+      if constexpr (kA8 && kEpi != EPI_SWIGLU) rbuf[mb & 1][it] = p.ascale[row];
+    }
+  };
+  if constexpr (kEpi == EPI_RESID) {
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(p.gate + col_base + lc);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(p.gate + col_base + lc + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      gsc[j] = g0[j] * csc[j];
+      gsc[4 + j] = g1[j] * csc[4 + j];
+    }
+  }
+  if constexpr (kEpi == EPI_RESID || (kA8 && kEpi != EPI_SWIGLU)) fetch_rows(0);
+  // QKV, q and k columns: a lane's 8 features lie in one RoPE chunk (axis, first pair k0); the
+  // table offsets of its rows are read once, the (cos, sin) entries one slice ahead.
+  const int region = kEpi == EPI_QKV ? static_cast<int>(n0 / p.d_model) : 0;  // 0 q, 1 k, 2 v
+  const int64_t fq = col_base + lc - static_cast<int64_t>(region) * p.d_model;  // first of 8 features
+  [[maybe_unused]] int rbase[4][kIt];
+  [[maybe_unused]] f32x4 csb[2][kIt][2];
+  auto fetch_rope = [&](int mb) {
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int64_t row = row_base + mb * 32 + it * kRowsPass + lr;
+      if (row < p.geom.n_video) {
+        csb[mb & 1][it][0] = *reinterpret_cast<const f32x4*>(p.rope.table + rbase[mb][it]);
+        csb[mb & 1][it][1] = *reinterpret_cast<const f32x4*>(p.rope.table + rbase[mb][it] + 2);
+      }
+    }
+  };
+  if constexpr (kEpi == EPI_QKV) {
+    if (region < 2) {
+      const int dh = static_cast<int>(fq % p.rope.head_dim);
+      const int ct = p.rope.head_dim / 4, cy = 3 * p.rope.head_dim / 8;
+      const int axis = dh < ct ? 0 : (dh < ct + cy ? 1 : 2);
+      const int k0 = axis == 0 ? dh / 2 : (axis == 1 ? (dh - ct) / 2 : (dh - ct - cy) / 2);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+          const int64_t row = row_base + mb * 32 + it * kRowsPass + lr;
+          rbase[mb][it] = row < p.geom.n_video ? reinterpret_cast<const int*>(p.rope.rowbase + row)[axis] + k0 : 0;
+        }
+      fetch_rope(0);
+    }
+  }
+  // SwiGLU: SN packed columns = SN/64 groups of [32 gate | 32 up] -> SN/2 h features per row;
+  // a lane owns 8 consecutive features (their gate and up columns) on kItH rows per slice.
+  constexpr int kLanesH = SN / 16, kRowsH = 64 / kLanesH, kItH = 32 / kRowsH;
+  const int hc = (lane % kLanesH) * 8;  // this lane's first h feature within the wave's SN/2
+  const int gcol = (hc / 32) * 64 + hc % 32, ucol = gcol + 32;
+  [[maybe_unused]] float sg[8], su[8], rsh[4][kItH];
+  if constexpr (kEpi == EPI_SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { sg[j] = 1.0f; su[j] = 1.0f; }
+    if constexpr (kInt8 || kA8) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(p.wscale + col_base + gcol);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(p.wscale + col_base + ucol);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sg[2 * j] = __uint_as_float(a[j] << 16); sg[2 * j + 1] = __uint_as_float(a[j] & 0xffff0000u);
+        su[2 * j] = __uint_as_float(b[j] << 16); su[2 * j + 1] = __uint_as_float(b[j] & 0xffff0000u);
+      }
+    }
+    if constexpr (kA8) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int it = 0; it < kItH; ++it) rsh[mb][it] = p.ascale[row_base + mb * 32 + it * kRowsH + lane / kLanesH];
+    }
+  }
 
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
+    if constexpr (kEpi == EPI_RESID || (kA8 && kEpi != EPI_SWIGLU))
+      if (mb + 1 < 4) fetch_rows(mb + 1);
+    if constexpr (kEpi == EPI_QKV)
+      if (region < 2 && mb + 1 < 4) fetch_rope(mb + 1);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -373,15 +468,15 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
     const int64_t r0 = row_base + mb * 32;
 
     if constexpr (kEpi == EPI_F32 || kEpi == EPI_RESID) {
-#pragma unroll 2
-      for (int it = 0; it < 32 / kRowsPass; ++it) {
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
         const int r = it * kRowsPass + lr;
         const int64_t row = r0 + r;
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc + 4);
         float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         if constexpr (kA8) {
-          const float rs = p.ascale[row];
+          const float rs = rbuf[mb & 1][it];
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] *= rs;
         }
@@ -392,16 +487,13 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
             *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4] * csc[4], v[5] * csc[5], v[6] * csc[6], v[7] * csc[7]};
           } else {
             uint16_t* xp = static_cast<uint16_t*>(p.x) + row * p.n + col_base + lc;
-            const u32x4 xr = *reinterpret_cast<const u32x4*>(xp);
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(p.gate + col_base + lc);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(p.gate + col_base + lc + 4);
-            const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+            const u32x4 xr = xbuf[mb & 1][it];
             u32x4 out;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float x0 = __uint_as_float(xr[j] << 16), x1 = __uint_as_float(xr[j] & 0xffff0000u);
-              const float y0 = fmaf(g[2 * j] * csc[2 * j], v[2 * j], x0);
-              const float y1 = fmaf(g[2 * j + 1] * csc[2 * j + 1], v[2 * j + 1], x1);
+              const float y0 = fmaf(gsc[2 * j], v[2 * j], x0);
+              const float y1 = fmaf(gsc[2 * j + 1], v[2 * j + 1], x1);
               out[j] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
                        (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
             }
@@ -410,27 +502,10 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
         }
       }
     } else if constexpr (kEpi == EPI_SWIGLU) {
-      // SN packed columns = SN/64 groups of [32 gate | 32 up] -> SN/2 h features per row.
-      constexpr int kLanesH = SN / 16, kRowsH = 64 / kLanesH;
-      const int hc = (lane % kLanesH) * 8;  // this lane's first h feature within the wave's SN/2
-      const int grp = hc / 32, ih = hc % 32;
-      const int gcol = grp * 64 + ih, ucol = gcol + 32;
-      float sg[8], su[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { sg[j] = 1.0f; su[j] = 1.0f; }
-      if constexpr (kInt8 || kA8) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(p.wscale + col_base + gcol);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(p.wscale + col_base + ucol);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sg[2 * j] = __uint_as_float(a[j] << 16); sg[2 * j + 1] = __uint_as_float(a[j] & 0xffff0000u);
-          su[2 * j] = __uint_as_float(b[j] << 16); su[2 * j + 1] = __uint_as_float(b[j] & 0xffff0000u);
-        }
-      }
       const int64_t F = p.n / 2;
       const int64_t f0 = col_base / 2 + hc;
-#pragma unroll 2
-      for (int it = 0; it < 32 / kRowsH; ++it) {
+#pragma unroll
+      for (int it = 0; it < kItH; ++it) {
         const int r = it * kRowsH + lane / kLanesH;
         const int64_t row = r0 + r;
         const f32x4 ga = *reinterpret_cast<const f32x4*>(st + r * kStride + gcol);
@@ -440,7 +515,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
         float gv[8] = {ga[0], ga[1], ga[2], ga[3], gb[0], gb[1], gb[2], gb[3]};
         float uv[8] = {ua[0], ua[1], ua[2], ua[3], ub[0], ub[1], ub[2], ub[3]};
         if constexpr (kA8) {
-          const float rs = p.ascale[row];
+          const float rs = rsh[mb][it];
 #pragma unroll
           for (int j = 0; j < 8; ++j) { gv[j] *= rs; uv[j] *= rs; }
         }
@@ -448,8 +523,8 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
           u32x4 out;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float h0 = silu(gv[2 * j] * sg[2 * j]) * (uv[2 * j] * su[2 * j]);
-            const float h1 = silu(gv[2 * j + 1] * sg[2 * j + 1]) * (uv[2 * j + 1] * su[2 * j + 1]);
+            const float h0 = silu_rcp(gv[2 * j] * sg[2 * j]) * (uv[2 * j] * su[2 * j]);
+            const float h1 = silu_rcp(gv[2 * j + 1] * sg[2 * j + 1]) * (uv[2 * j + 1] * su[2 * j + 1]);
             out[j] = static_cast<uint32_t>(f32_to_bf16_bits(h0)) |
                      (static_cast<uint32_t>(f32_to_bf16_bits(h1)) << 16);
           }
@@ -461,16 +536,11 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
       }
     } else {  // EPI_QKV
       const int64_t d = p.d_model;
-      const int region = static_cast<int>(n0 / d);  // 0 = q, 1 = k, 2 = v (d % 256 == 0)
       if (region < 2) {
         uint16_t* dst = static_cast<uint16_t*>(region == 0 ? p.q : p.kk);
-        const int64_t f = col_base + lc - region * d;        // first of 8 features
-        const int dh = static_cast<int>(f % p.rope.head_dim);  // the 8 lie in one RoPE chunk
-        const int ct = p.rope.head_dim / 4, cy = 3 * p.rope.head_dim / 8;
-        const int axis = dh < ct ? 0 : (dh < ct + cy ? 1 : 2);
-        const int k0 = axis == 0 ? dh / 2 : (axis == 1 ? (dh - ct) / 2 : (dh - ct - cy) / 2);
-#pragma unroll 2
-        for (int it = 0; it < 32 / kRowsPass; ++it) {
+        const int64_t f = fq;
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
           const int r = it * kRowsPass + lr;
           const int64_t row = r0 + r;
           const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc);
@@ -478,15 +548,13 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
           float v[8] = {v0[0] * csc[0], v0[1] * csc[1], v0[2] * csc[2], v0[3] * csc[3],
                         v1[0] * csc[4], v1[1] * csc[5], v1[2] * csc[6], v1[3] * csc[7]};
           if constexpr (kA8) {
-            const float rs = p.ascale[row];
+            const float rs = rbuf[mb & 1][it];
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] *= rs;
           }
           if (row < p.geom.n_video) {
-            const int4 rb = p.rope.rowbase[row];
-            const int base = (axis == 0 ? rb.x : (axis == 1 ? rb.y : rb.z)) + k0;
-            const f32x4 cs01 = *reinterpret_cast<const f32x4*>(p.rope.table + base);
-            const f32x4 cs23 = *reinterpret_cast<const f32x4*>(p.rope.table + base + 2);
+            const f32x4 cs01 = csb[mb & 1][it][0];
+            const f32x4 cs23 = csb[mb & 1][it][1];
             const float c[4] = {cs01[0], cs01[2], cs23[0], cs23[2]};
             const float sn[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
 #pragma unroll
