@@ -2,7 +2,8 @@
  * h3x_kernels.h -- kernel-level entry points of libh3x: one step of the block or the sampler
  * per call, for per-kernel parity tests and per-kernel timing. Same conventions as h3x.h
  * (device pointers named "dev", caller-owned buffers, asynchronous on `stream`, validation
- * before any launch, status codes, no allocation).
+ * before any launch, status codes, no allocation). A call with zero rows (n_rows, m) is valid,
+ * enqueues nothing and does not look at its data pointers (they may be NULL).
  *
  * Internal attention layouts used by these entry points, for a sequence of N tokens and
  * Npad = N rounded up to a multiple of 256:

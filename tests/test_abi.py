@@ -236,3 +236,22 @@ def test_status_strings(B):
     assert L.h3x_status_string(0) == b"ok"
     assert L.h3x_status_string(3) == b"workspace too small"
     assert L.h3x_copy(FAKE, FAKE, 17, None) == 1
+
+
+def test_zero_row_calls_enqueue_nothing(B):
+    """Zero rows: valid, nothing enqueued, pointers not looked at (no device needed)."""
+    L = B.lib()
+    c = _cfg(B)
+    ca = _cfg(B, weight="i8a8")
+    assert L.h3x_norm_mod(ctypes.byref(c), 0, None, None, None, None, None) == 0
+    assert L.h3x_linear_f32out(ctypes.byref(c), 1, 0, None, None, None, None, None) == 0
+    assert L.h3x_linear_residual(ctypes.byref(c), 3, 0, None, None, None, None, None, None) == 0
+    assert L.h3x_linear_swiglu(ctypes.byref(c), 0, None, None, None, None, None) == 0
+    assert L.h3x_euler(ctypes.byref(c), 0, None, None, 1.0, 0.5, None, None) == 0
+    assert L.h3x_quant_rows(0, 64, None, None, None, None) == 0
+    assert L.h3x_norm_mod_quant(ctypes.byref(ca), 0, None, None, None, None, None, None) == 0
+    assert L.h3x_linear_a8_f32out(ctypes.byref(ca), 1, 0, None, None, None, None, None, None) == 0
+    # The row count is still range-checked, and the other arguments still validated.
+    assert L.h3x_norm_mod(ctypes.byref(c), -1, None, None, None, None, None) == 1
+    assert L.h3x_quant_rows(0, 100, None, None, None, None) == 1
+    assert L.h3x_linear_f32out(ctypes.byref(c), 7, 0, None, None, None, None, None) == 1

@@ -202,3 +202,47 @@ def test_block_strong_vs_storage_rounded(B, record):
     e = rel_l2(host(xd), ref)
     record("block_strong_vs_storage_rounded", e, 1e-2)
     assert e < 1e-2
+
+
+# ---------------------------------------------------------------- degenerate sizes
+@pytest.mark.parametrize("weight", ["bf16", "i8a8"])
+@pytest.mark.parametrize("geom", [(0, 0, 0, 0, 1), (0, 0, 0, 3, 2), (1, 1, 2, 0, 0)],
+                         ids=["one_text_token", "audio_text_only", "two_video_tokens"])
+def test_block_tiny_sequences(B, weight, geom, record):
+    """Sequences of one to five tokens (no video axis at all, or a single latent row): a single
+    key makes attention return v exactly, and every tile is almost all padding."""
+    wl = SMALL.replace(name=f"tiny_seq_{weight}", weight=weight, frames=geom[0], grid_h=geom[1],
+                       grid_w=geom[2], n_audio=geom[3], n_text=geom[4], seed_base=16)
+    og = oracle_geom(wl)
+    x = synth.storage_values(synth.normal(wl.seed_base, 5, (og.n_tokens, wl.d_model)), "bf16")
+    xd, w64, m64 = run_block(B, wl, x)
+    aq = None
+    if weight == "i8a8":
+        from oracle import quant
+        aq = quant.w8a8_act("bf16")
+    ref = dit.block_forward(x, w64, m64, og, wl.n_heads, act_quant=aq)
+    e = rel_l2(host(xd), ref)
+    record(f"block_tiny_sequence[{weight},{geom}]", e, _tol(wl))
+    assert e < _tol(wl)
+
+
+def test_empty_inputs_are_no_ops(B):
+    """Zero rows through every kernel-level entry point that takes a row count: nothing is
+    launched, nothing fails."""
+    wl = SMALL
+    cfg = binding_cfg(wl)
+    d, f = wl.d_model, wl.ffn_inner
+    x = torch.empty(0, d, dtype=torch.bfloat16, device="cuda")
+    sh = torch.zeros(d, dtype=torch.float32, device="cuda")
+    assert B.norm_mod(cfg, x, sh, sh).shape == (0, d)
+    w = B.pack_weights(cfg, B.W_OUT, torch.zeros(d, d, dtype=torch.bfloat16, device="cuda"))
+    assert B.linear_f32out(cfg, B.W_OUT, x, w).shape == (0, d)
+    B.linear_residual(cfg, B.W_OUT, x, w, None, sh, x)
+    z = torch.empty(0, d, dtype=torch.float32, device="cuda")
+    B.euler(cfg, z, x, 1.0, 0.5)
+    q, s = B.quant_rows(x)
+    cfg8 = binding_cfg(wl.replace(weight="i8a8"))
+    qw, sw = B.pack_int8_weights(cfg8, B.W_OUT, torch.zeros(d, d, dtype=torch.bfloat16, device="cuda"))
+    assert B.linear_a8_f32out(cfg8, B.W_OUT, 0, q, s, qw, sw).shape == (0, d)
+    B.norm_mod_quant(cfg8, x, sh, sh)
+    torch.cuda.synchronize()

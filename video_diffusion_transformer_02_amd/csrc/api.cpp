@@ -629,6 +629,7 @@ h3x_status h3x_norm_mod(const h3x_block_cfg* c, int64_t n_rows, const void* x, c
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
   if (n_rows < 0) return fail(H3X_EINVAL, "norm_mod: n_rows < 0");
+  if (n_rows == 0) return H3X_OK;
   if (!x || !shift || !scale || !y || !aligned16(x) || !aligned16(y) || !aligned16(shift) || !aligned16(scale))
     return fail(H3X_EINVAL, "norm_mod: NULL or misaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -698,8 +699,9 @@ static h3x_status linear_common(const h3x_block_cfg* c, int32_t kind, int64_t m,
   if (st != H3X_OK) return st;
   if (kind < H3X_W_QKV || kind > H3X_W_DOWN) return fail(H3X_EINVAL, "linear: bad kind");
   if (m < 0 || m > (int64_t(1) << 26)) return fail(H3X_EINVAL, "linear: bad m");
-  if (!a || !w || !aligned16(a) || !aligned16(w)) return fail(H3X_EINVAL, "linear: NULL or misaligned pointer");
   if (c->weight == H3X_I8A8) return fail(H3X_ENOTSUP, "linear: I8A8 takes quantised activations (h3x_linear_a8_f32out)");
+  if (m == 0) return H3X_OK;  // nothing to do; the callers return before looking at pointers
+  if (!a || !w || !aligned16(a) || !aligned16(w)) return fail(H3X_EINVAL, "linear: NULL or misaligned pointer");
   if ((c->weight == H3X_I8) != (sc != nullptr)) return fail(H3X_EINVAL, "linear: scales iff int8 weights");
   return H3X_OK;
 }
@@ -707,6 +709,7 @@ static h3x_status linear_common(const h3x_block_cfg* c, int32_t kind, int64_t m,
 h3x_status h3x_quant_rows(int64_t m, int64_t cols, const void* a, void* q, float* sc, void* stream) {
   if (m < 0 || m > (int64_t(1) << 26)) return fail(H3X_EINVAL, "quant_rows: bad m");
   if (cols <= 0 || cols % 64 || cols > 32768) return fail(H3X_EINVAL, "quant_rows: need 0 < cols <= 32768, cols % 64 == 0");
+  if (m == 0) return H3X_OK;
   if (!a || !q || !sc || !aligned16(a) || !aligned16(q) || !aligned16(sc))
     return fail(H3X_EINVAL, "quant_rows: NULL or misaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -720,6 +723,7 @@ h3x_status h3x_norm_mod_quant(const h3x_block_cfg* c, int64_t n_rows, const void
   if (st != H3X_OK) return st;
   if (c->weight != H3X_I8A8) return fail(H3X_EINVAL, "norm_mod_quant: cfg->weight must be I8A8");
   if (n_rows < 0 || n_rows > (int64_t(1) << 26)) return fail(H3X_EINVAL, "norm_mod_quant: bad n_rows");
+  if (n_rows == 0) return H3X_OK;
   if (!x || !shift || !scale || !q || !sc || !aligned16(x) || !aligned16(shift) || !aligned16(scale) ||
       !aligned16(q) || !aligned16(sc))
     return fail(H3X_EINVAL, "norm_mod_quant: NULL or misaligned pointer");
@@ -736,6 +740,7 @@ h3x_status h3x_linear_a8_f32out(const h3x_block_cfg* c, int32_t kind, int64_t m,
   if (c->weight != H3X_I8A8) return fail(H3X_EINVAL, "linear_a8_f32out: cfg->weight must be I8A8");
   if (kind < H3X_W_QKV || kind > H3X_W_DOWN) return fail(H3X_EINVAL, "linear_a8_f32out: bad kind");
   if (m < 0 || m > (int64_t(1) << 26)) return fail(H3X_EINVAL, "linear_a8_f32out: bad m");
+  if (m == 0) return H3X_OK;
   if (!qa || !sa || !w || !sw || !out || !aligned16(qa) || !aligned16(sa) || !aligned16(w) || !aligned16(out))
     return fail(H3X_EINVAL, "linear_a8_f32out: NULL or misaligned pointer");
   GemmArgs g = gemm_args(c, kind, m, qa, w, sw);
@@ -750,7 +755,7 @@ h3x_status h3x_linear_a8_f32out(const h3x_block_cfg* c, int32_t kind, int64_t m,
 h3x_status h3x_linear_residual(const h3x_block_cfg* c, int32_t kind, int64_t m, const void* a, const void* w,
                                const void* sc, const float* gate, void* x, void* stream) {
   h3x_status st = linear_common(c, kind, m, a, w, sc);
-  if (st != H3X_OK) return st;
+  if (st != H3X_OK || m == 0) return st;
   if (kind != H3X_W_OUT && kind != H3X_W_DOWN) return fail(H3X_EINVAL, "linear_residual: kind must be OUT or DOWN");
   if (!gate || !x || !aligned16(x)) return fail(H3X_EINVAL, "linear_residual: NULL or misaligned gate / x");
   GemmArgs g = gemm_args(c, kind, m, a, w, sc);
@@ -763,7 +768,7 @@ h3x_status h3x_linear_residual(const h3x_block_cfg* c, int32_t kind, int64_t m, 
 h3x_status h3x_linear_swiglu(const h3x_block_cfg* c, int64_t m, const void* y2, const void* w, const void* sc,
                              void* h, void* stream) {
   h3x_status st = linear_common(c, H3X_W_GATE_UP, m, y2, w, sc);
-  if (st != H3X_OK) return st;
+  if (st != H3X_OK || m == 0) return st;
   if (!h || !aligned16(h)) return fail(H3X_EINVAL, "linear_swiglu: NULL or misaligned h");
   GemmArgs g = gemm_args(c, H3X_W_GATE_UP, m, y2, w, sc);
   g.h = h;
@@ -775,7 +780,7 @@ h3x_status h3x_linear_swiglu(const h3x_block_cfg* c, int64_t m, const void* y2, 
 h3x_status h3x_linear_f32out(const h3x_block_cfg* c, int32_t kind, int64_t m, const void* a, const void* w,
                              const void* sc, float* out, void* stream) {
   h3x_status st = linear_common(c, kind, m, a, w, sc);
-  if (st != H3X_OK) return st;
+  if (st != H3X_OK || m == 0) return st;
   if (!out || !aligned16(out)) return fail(H3X_EINVAL, "linear_f32out: NULL or misaligned out");
   GemmArgs g = gemm_args(c, kind, m, a, w, sc);
   g.out = out;
@@ -811,6 +816,7 @@ h3x_status h3x_euler(const h3x_block_cfg* c, int64_t n_rows, float* z, const voi
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
   if (n_rows < 0) return fail(H3X_EINVAL, "euler: n_rows < 0");
+  if (n_rows == 0) return H3X_OK;
   if (!isfinite(sigma) || !isfinite(sigma_next)) return fail(H3X_EINVAL, "euler: non-finite sigma");
   if (!z || !v || !aligned16(z) || !aligned16(v) || (v_copy && !aligned16(v_copy)))
     return fail(H3X_EINVAL, "euler: NULL or misaligned pointer");

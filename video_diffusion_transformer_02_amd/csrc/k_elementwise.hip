@@ -728,6 +728,7 @@ hipError_t launch_rope_table(const GeomDev& g, int head_dim, float theta, float2
                              int4* rowbase, hipStream_t s) {
   const int kt = head_dim / 8, ky = 3 * head_dim / 16;
   const int n = g.frames * kt + g.grid_h * ky + 2 * g.grid_w * ky;
+  if (n == 0) return hipSuccess;  // no video axis at all (audio / text only)
   rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(table, g.frames, g.grid_h, g.grid_w, kt, ky,
                                                     log2(static_cast<double>(theta)));
   hipError_t e = hipGetLastError();
