@@ -90,6 +90,25 @@ def measured_traffic(path):
     return float(fields["traffic_bytes_per_launch"])
 
 
+def measure_copy(B, torch, nbytes=1 << 30, reps=10):
+    """Device copy rate (read + write bytes per second, GB/s): the practical HBM ceiling the
+    memory-bound kernels are compared with."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        B.copy(src, dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        B.copy(src, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / ms / 1e6
+
+
 def bench_block(args, B, torch, synth, weight="bf16"):
     w = synth.BLOCK
     cfg = B.BlockCfg.make(w.d_model, w.n_heads, w.head_dim, w.ffn_inner, "bf16", weight)
@@ -355,6 +374,11 @@ def main():
         print(json.dumps({"ms_per_step": ms, "weights": args.block_weight, "kernels": kern}))
         return
     ms, flops, kern, roof, state = bench_block(args, B, torch, synth)
+    copy_gbs = measure_copy(B, torch)
+    log(f"[bench] device copy {copy_gbs:.0f} GB/s (read + write)")
+    for name in ("norm_mod", "norm_mod_quant"):
+        if name in kern and "gbs" in kern[name]:
+            kern[name]["frac_copy"] = round(kern[name]["gbs"] / copy_gbs, 3)
     w8a8 = None
     if not args.no_w8a8:
         ms8, _, kern8, roof8, _ = bench_block(args, B, torch, synth, "i8a8")
@@ -381,6 +405,7 @@ def main():
                    "ffn_inner": w.ffn_inner, "tokens": w.n_tokens, "block_flops": flops},
         "frac_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
+        "hbm_copy_gbs": round(copy_gbs, 1),
         "cpu_baseline": cpu,
         "kernels": kern,
         "block_w8a8": w8a8,

@@ -255,3 +255,16 @@ def test_zero_row_calls_enqueue_nothing(B):
     assert L.h3x_norm_mod(ctypes.byref(c), -1, None, None, None, None, None) == 1
     assert L.h3x_quant_rows(0, 100, None, None, None, None) == 1
     assert L.h3x_linear_f32out(ctypes.byref(c), 7, 0, None, None, None, None, None) == 1
+
+
+def test_sequence_length_limit(B):
+    """bf16 K and V^T matrices are addressed with 32-bit buffer offsets: Npad * d * 2 < 2^31."""
+    L = B.lib()
+    c = _cfg(B, d_model=6144, n_heads=48, ffn_inner=24576)
+    g = B.Geom(1, 400, 500, 0, 0, 0)  # 200000 tokens
+    st = L.h3x_dit_block_forward(ctypes.byref(c), ctypes.byref(g), None, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == 2, _last(B)
+    assert L.h3x_attention(ctypes.byref(c), 200000, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == 2
+    # The largest sequence that fits still passes this check (and fails later for other reasons).
+    n_ok = (2 ** 31 - 1) // (6144 * 2) // 256 * 256
+    assert L.h3x_attention(ctypes.byref(c), n_ok, None, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, None) == 1

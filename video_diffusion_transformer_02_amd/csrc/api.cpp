@@ -128,6 +128,14 @@ h3x_status check_geom(const h3x_geom* g) {
   return H3X_OK;
 }
 
+// The bfloat16 attention addresses K and V^T of a sequence through 32-bit buffer offsets: one
+// head-major K or V^T matrix of Npad x d bfloat16 must stay below 2^31 bytes.
+h3x_status check_seq(const h3x_block_cfg* c, int64_t n) {
+  if (c->act == H3X_BF16 && ((n + 255) / 256 * 256) * static_cast<int64_t>(c->d_model) * 2 > INT32_MAX)
+    return fail(H3X_ENOTSUP, "sequence too long: Npad * d_model * 2 must stay below 2^31 bytes");
+  return H3X_OK;
+}
+
 int64_t geom_tokens(const h3x_geom* g) {
   const int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h * g->grid_w;
   return (g->merged ? nv / 2 : nv) + g->n_audio + g->n_text;
@@ -457,6 +465,7 @@ h3x_status h3x_dit_block_forward(const h3x_block_cfg* c, const h3x_geom* g, cons
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
   if ((st = check_geom(g)) != H3X_OK) return st;
+  if ((st = check_seq(c, geom_tokens(g))) != H3X_OK) return st;
   if ((st = check_weights(c, w)) != H3X_OK) return st;
   if (!mod || !x || !ws || !aligned16(mod) || !aligned16(x) || !aligned16(ws))
     return fail(H3X_EINVAL, "block_forward: NULL or misaligned mod / x / ws");
@@ -509,6 +518,7 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
   if (st != H3X_OK) return st;
   if ((st = check_geom(g)) != H3X_OK) return st;
   if (g->merged) return fail(H3X_EINVAL, "denoise_step: geom must be unmerged");
+  if ((st = check_seq(c, geom_tokens(g))) != H3X_OK) return st;
   if (!st_) return fail(H3X_EINVAL, "denoise_step: step is NULL");
   const int fresh = h3x_step_is_fresh(st_->step, st_->n_steps, st_->reuse);
   if (fresh < 0) return fail(H3X_EINVAL, "denoise_step: need 0 <= step < n_steps and reuse >= 1");
@@ -680,6 +690,7 @@ h3x_status h3x_attention(const h3x_block_cfg* c, int64_t n_tokens, const void* q
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
   if (n_tokens < 1 || n_tokens > (int64_t(1) << 26)) return fail(H3X_EINVAL, "attention: bad n_tokens");
+  if ((st = check_seq(c, n_tokens)) != H3X_OK) return st;
   if (slots < 0) return fail(H3X_EINVAL, "attention: negative slots");
   if (!q || !k || !vt || !o || !aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
     return fail(H3X_EINVAL, "attention: NULL or misaligned pointer");
