@@ -83,7 +83,10 @@ typedef struct {
 } h3x_block_cfg;
 
 /* Latent geometry of the joint sequence. frames x grid_h x grid_w video tokens (halved when
- * merged == 1; grid_w must then be even), then n_audio, then n_text tokens. */
+ * merged == 1; grid_w must then be even), then n_audio, then n_text tokens. With bfloat16
+ * activations the entry points that run attention return H3X_ENOTSUP when
+ * round_up(N, 256) * d_model * 2 reaches 2^31 bytes (the K and V^T matrices are addressed with
+ * 32-bit offsets): about 174k tokens at d_model 6144. */
 typedef struct {
   int32_t frames, grid_h, grid_w, n_audio, n_text;
   int32_t merged;
