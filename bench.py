@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--block-weight", default="bf16", choices=["bf16", "i8", "i8a8"],
                    help="weight type of the block timed with --only-block")
     p.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 block and schedule")
+    p.add_argument("--only-sampler", action="store_true",
+                   help="the memory-bound kernels alone at the block shape (for profilers)")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run a 1 GiB device copy (byte-counter calibration)")
     return p.parse_args()
@@ -93,8 +95,9 @@ def measured_traffic(path):
 def measure_copy(B, torch, nbytes=1 << 30, reps=10):
     """Device copy rate (read + write bytes per second, GB/s): the practical HBM ceiling the
     memory-bound kernels are compared with."""
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
+    # Both buffers written first, so that every page is backed before it is counted.
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
     for _ in range(2):
         B.copy(src, dst)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -142,8 +145,8 @@ def bench_block(args, B, torch, synth, weight="bf16"):
     log(f"[bench] block {ms:.3f} ms  {flops / ms / 1e9:.1f} TFLOP/s")
     if args.copy_calib:
         # A plain copy of known size, for calibrating hardware byte counters.
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.zeros_like(src)
         for _ in range(3):
             B.copy(src, dst)
         torch.cuda.synchronize()
@@ -180,6 +183,52 @@ def bench_block(args, B, torch, synth, weight="bf16"):
             "traffic": traffic, "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": dom_ms}
     state = {"raw": raw, "mod": mod, "x": x_host, "w": w}
     return ms, flops, kern, roof, state
+
+
+def bench_sampler(args, B, torch, synth):
+    """The memory-bound kernels of the path at the 6 x 32 x 32 + 256 + 512 token, d = 6144 shape:
+    modulated RMSNorm, token merge and unmerge (blocks 10..34), the fresh Euler step with the
+    velocity-cache write and the reused step; ms and GB/s of their algorithmic bytes."""
+    w = synth.BLOCK
+    cfg = B.BlockCfg.make(w.d_model, w.n_heads, w.head_dim, w.ffn_inner, "bf16", "bf16")
+    g = B.Geom(w.frames, w.grid_h, w.grid_w, w.n_audio, w.n_text, 0)
+    n, d = g.n_tokens, w.d_model
+    nm = g.as_merged().n_tokens
+    ns = w.n_state
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn(n, d, generator=gen, device="cuda").to(torch.bfloat16)
+    z = torch.randn(ns, d, generator=gen, device="cuda")
+    v = torch.randn(ns, d, generator=gen, device="cuda").to(torch.bfloat16)
+    vc = torch.empty_like(v)
+    mod = torch.from_numpy(synth.modulation(w, 0, 0)).cuda()
+    y = torch.empty_like(x)
+    xm = B.token_merge(cfg, g, x)
+    xu = B.token_unmerge(cfg, g, xm)
+    if args.copy_calib:
+        measure_copy(B, torch, reps=3)
+    runs = {
+        "norm_mod": (lambda: B.norm_mod(cfg, x, mod[0], mod[1], y), 2.0 * n * d * 2),
+        "token_merge": (lambda: B.token_merge(cfg, g, x), (n + nm) * d * 2.0),
+        "token_unmerge": (lambda: B.token_unmerge(cfg, g, xm), (n + nm) * d * 2.0),
+        "euler_fresh": (lambda: B.euler(cfg, z, v, 1.0, 0.95, vc), ns * d * (8.0 + 2 + 2)),
+        "euler_reused": (lambda: B.euler(cfg, z, v, 0.95, 0.9), ns * d * (8.0 + 2)),
+    }
+    out = {}
+    for name, (fn, nbytes) in runs.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        B.profile_begin()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        prof = B.profile_end()
+        launches, total = next(iter(prof.values()))
+        ms = total / launches
+        out[name] = {"avg_ms": round(ms, 5), "algorithmic_bytes": nbytes, "gbs": round(nbytes / ms / 1e6, 1)}
+        log(f"[bench] {name:14s} {ms:.4f} ms  {nbytes / ms / 1e6:7.1f} GB/s")
+    del xu
+    return out
 
 
 def cpu_baseline(args, state):
@@ -369,6 +418,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     B.lib()
+    if args.only_sampler:
+        print(json.dumps({"sampler_kernels": bench_sampler(args, B, torch, synth)}))
+        return
     if args.only_block:
         ms, flops, kern, roof, state = bench_block(args, B, torch, synth, args.block_weight)
         print(json.dumps({"ms_per_step": ms, "weights": args.block_weight, "kernels": kern}))
@@ -376,6 +428,9 @@ def main():
     ms, flops, kern, roof, state = bench_block(args, B, torch, synth)
     copy_gbs = measure_copy(B, torch)
     log(f"[bench] device copy {copy_gbs:.0f} GB/s (read + write)")
+    sampler = bench_sampler(args, B, torch, synth)
+    for e in sampler.values():
+        e["frac_copy"] = round(e["gbs"] / copy_gbs, 3)
     for name in ("norm_mod", "norm_mod_quant"):
         if name in kern and "gbs" in kern[name]:
             kern[name]["frac_copy"] = round(kern[name]["gbs"] / copy_gbs, 3)
@@ -406,6 +461,7 @@ def main():
         "frac_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "hbm_copy_gbs": round(copy_gbs, 1),
+        "sampler_kernels": sampler,
         "cpu_baseline": cpu,
         "kernels": kern,
         "block_w8a8": w8a8,

@@ -366,15 +366,22 @@ __global__ __launch_bounds__(kThreads) void unmerge_kernel(const typename E::T* 
                                                            typename E::T* __restrict__ x,
                                                            int64_t n_video, int64_t n_out,
                                                            int d) {
+  // One lane per 16-byte chunk of a merged row, read once: a video pair's chunk is written to
+  // both rows of the pair.
   constexpr int V = Vec<E>::n;
   const int64_t cpr = d / V;
-  const int64_t total = n_out * cpr;
+  const int64_t nv_half = n_video / 2;
+  const int64_t total = (n_out - nv_half) * cpr;  // merged rows
   for (int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * kThreads) {
-    const int64_t row = idx / cpr, c = (idx % cpr) * V;
-    const int64_t src = row < n_video ? row / 2 : row - n_video / 2;
-    const uint4 raw = *reinterpret_cast<const uint4*>(xm + src * d + c);
-    *reinterpret_cast<uint4*>(x + row * d + c) = raw;
+    const int64_t p = idx / cpr, c = (idx % cpr) * V;
+    const uint4 raw = *reinterpret_cast<const uint4*>(xm + p * d + c);
+    if (p < nv_half) {
+      *reinterpret_cast<uint4*>(x + (2 * p) * d + c) = raw;
+      *reinterpret_cast<uint4*>(x + (2 * p + 1) * d + c) = raw;
+    } else {
+      *reinterpret_cast<uint4*>(x + (p + nv_half) * d + c) = raw;
+    }
   }
 }
 
@@ -657,7 +664,7 @@ hipError_t launch_token_unmerge(int act, const GeomDev& g, int d, const void* xm
                                 hipStream_t s) {
   const int64_t n_out = g.n_video + g.n_audio + g.n_text;
   const int V = act == H3X_BF16 ? 8 : 4;
-  const int grid = grid_for(n_out * (d / V));
+  const int grid = grid_for((n_out - g.n_video / 2) * (d / V));
   if (act == H3X_BF16)
     unmerge_kernel<BF16><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(xm),
                                                    static_cast<uint16_t*>(x), g.n_video, n_out, d);
