@@ -214,6 +214,9 @@ def test_workspace_and_packing_sizes(B):
     assert L.h3x_packed_scale_count(ctypes.byref(ca), 2) == 2 * 24576
     wa = L.h3x_block_workspace_bytes(ctypes.byref(ca), ctypes.byref(g))
     assert wa - ws == 6912 * 24576 + 6912 * 4
+    # int8 weights (W8A16): room to widen the largest matrix (gate/up, 2F x d) to bfloat16.
+    w8 = L.h3x_block_workspace_bytes(ctypes.byref(c8), ctypes.byref(g))
+    assert w8 - ws == 2 * 24576 * 6144 * 2
 
 
 def test_w8a8_kernel_level_contract(B):

@@ -174,6 +174,7 @@ struct BlockWs {
   uint8_t* attn;   // partial results of key-split attention workgroups
   uint8_t* a8;     // W8A8: int8 codes of the current projection input, [n_pad x max(d, F)] slabs
   float* a8s;      // W8A8: their float32 row scales [n_pad]
+  uint8_t* w16;    // int8 weights: one weight matrix widened to bfloat16 ahead of its GEMM
   size_t bytes;
 };
 
@@ -205,10 +206,16 @@ BlockWs block_layout(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* base) {
   w.attn = base + off; off = align256(off + attn_region_bytes(c, w.n));
   w.a8 = nullptr;
   w.a8s = nullptr;
+  w.w16 = nullptr;
   if (c->weight == H3X_I8A8) {
     const size_t cols = static_cast<size_t>(c->ffn_inner > c->d_model ? c->ffn_inner : c->d_model);
     w.a8 = base + off; off = align256(off + static_cast<size_t>(w.n_pad) * cols);
     w.a8s = reinterpret_cast<float*>(base + off); off = align256(off + static_cast<size_t>(w.n_pad) * 4);
+  }
+  if (c->weight == H3X_I8) {
+    const size_t d = c->d_model, f = c->ffn_inner;
+    const size_t most = 3 * d * d > 2 * f * d ? 3 * d * d : 2 * f * d;  // the largest matrix
+    w.w16 = base + off; off = align256(off + most * 2);
   }
   w.bytes = off;
   return w;
@@ -319,34 +326,56 @@ h3x_status block_forward_impl(const h3x_block_cfg* c, const h3x_geom* g, const h
 
   // bf16: the GEMM A operands (y, o, y2, h) live in the slab layout of the MFMA GEMM.
   const int tiled = c->act == H3X_BF16 ? 1 : 0;
+  // int8 weights: each matrix is widened to bfloat16 (exact) just before its GEMM, which then runs
+  // the bf16 kernel with the row scales in its epilogue. Widening inside the GEMM's K loop costs
+  // VALU work that the SIMDs cannot overlap with their MFMAs; this costs one pass over the codes.
+  const int wd = c->weight == H3X_I8 ? H3X_BF16 : c->weight;
+  hipError_t widen_err = hipSuccess;
+  auto widened = [&](int kind, const void* wq) -> const void* {
+    if (c->weight != H3X_I8) return wq;
+    int64_t rows, cols;
+    weight_shape(c, kind, &rows, &cols);
+    Timed _t("widen_int8", s);
+    widen_err = launch_widen_int8(rows, cols, static_cast<const int8_t*>(wq), ws.w16, s);
+    return widen_err == hipSuccess ? ws.w16 : nullptr;
+  };
+  auto widen_failed = [&]() { return hip_check(widen_err, "widen_int8"); };
   H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n, c->d_model, c->norm_eps, x, shift1, scale1, ws.y, tiled, s));
 
-  GemmArgs qa = gemm_args(c, H3X_W_QKV, n, ws.y, w->qkv, w->s_qkv);
+  const void* wqkv = widened(H3X_W_QKV, w->qkv);
+  if (!wqkv) return widen_failed();
+  GemmArgs qa = gemm_args(c, H3X_W_QKV, n, ws.y, wqkv, w->s_qkv);
   qa.a_tiled = tiled;
   qa.m_pad = ws.n_pad;
   qa.q = ws.q; qa.kk = ws.k; qa.vt = ws.vt; qa.geom = gd; qa.rope = rd;
-  H3X_LAUNCH(gemm_name(EPI_QKV), s, launch_gemm(c->act, c->weight, EPI_QKV, qa, s));
+  H3X_LAUNCH(gemm_name(EPI_QKV), s, launch_gemm(c->act, wd, EPI_QKV, qa, s));
 
   H3X_LAUNCH("attention", s, launch_attention(c->act, n, ws.n_pad, c->n_heads, c->head_dim, ws.q, ws.k, ws.vt, ws.o, tiled,
                                               attention_slots(0), ws.attn, s));
 
-  GemmArgs oa = gemm_args(c, H3X_W_OUT, n, ws.o, w->out, w->s_out);
+  const void* wout = widened(H3X_W_OUT, w->out);
+  if (!wout) return widen_failed();
+  GemmArgs oa = gemm_args(c, H3X_W_OUT, n, ws.o, wout, w->s_out);
   oa.a_tiled = tiled;
   oa.x = x; oa.gate = gate1;
-  H3X_LAUNCH("gemm_out_resid", s, launch_gemm(c->act, c->weight, EPI_RESID, oa, s));
+  H3X_LAUNCH("gemm_out_resid", s, launch_gemm(c->act, wd, EPI_RESID, oa, s));
 
   H3X_LAUNCH("norm_mod", s, launch_norm_mod(c->act, n, c->d_model, c->norm_eps, x, shift2, scale2, ws.y, tiled, s));
 
-  GemmArgs ga = gemm_args(c, H3X_W_GATE_UP, n, ws.y, w->gate_up, w->s_gate_up);
+  const void* wgu = widened(H3X_W_GATE_UP, w->gate_up);
+  if (!wgu) return widen_failed();
+  GemmArgs ga = gemm_args(c, H3X_W_GATE_UP, n, ws.y, wgu, w->s_gate_up);
   ga.a_tiled = tiled;
   ga.out_tiled = tiled;
   ga.h = ws.h;
-  H3X_LAUNCH(gemm_name(EPI_SWIGLU), s, launch_gemm(c->act, c->weight, EPI_SWIGLU, ga, s));
+  H3X_LAUNCH(gemm_name(EPI_SWIGLU), s, launch_gemm(c->act, wd, EPI_SWIGLU, ga, s));
 
-  GemmArgs da = gemm_args(c, H3X_W_DOWN, n, ws.h, w->down, w->s_down);
+  const void* wdn = widened(H3X_W_DOWN, w->down);
+  if (!wdn) return widen_failed();
+  GemmArgs da = gemm_args(c, H3X_W_DOWN, n, ws.h, wdn, w->s_down);
   da.a_tiled = tiled;
   da.x = x; da.gate = gate2;
-  H3X_LAUNCH("gemm_down_resid", s, launch_gemm(c->act, c->weight, EPI_RESID, da, s));
+  H3X_LAUNCH("gemm_down_resid", s, launch_gemm(c->act, wd, EPI_RESID, da, s));
   return H3X_OK;
 }
 
@@ -618,6 +647,7 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
       m.attn = lay.blk.attn;
       m.a8 = lay.blk.a8;
       m.a8s = lay.blk.a8s;
+      m.w16 = lay.blk.w16;
       bw = m;
     }
     if ((st = block_forward_impl(c, gb, &st_->blocks[b], st_->mod + b * mod_stride,

@@ -608,6 +608,31 @@ __global__ __launch_bounds__(kThreads) void pack_int8_kernel(const uint16_t* __r
   }
 }
 
+// int8 codes in slab_offset_i8 order -> the same values as bfloat16 in slab_offset order (exact:
+// |q| <= 127). One lane per 16-byte output chunk, in output order: a 16 KB bf16 slab is written
+// linearly while its 8 KB int8 slab is read once.
+__global__ __launch_bounds__(kThreads) void widen_int8_kernel(const int8_t* __restrict__ q,
+                                                              uint16_t* __restrict__ w,
+                                                              int64_t rows, int64_t cols) {
+  const int64_t total = rows * cols / 8;  // 16-byte output chunks
+  const int64_t kslabs = cols / 32;
+  for (int64_t o = blockIdx.x * (int64_t)kThreads + threadIdx.x; o < total; o += (int64_t)gridDim.x * kThreads) {
+    const int64_t slab = o >> 10;                  // 1024 chunks per 16 KB slab
+    const int rr = static_cast<int>((o >> 2) & 255), pc = static_cast<int>(o & 3);
+    const int lc = pc ^ ((rr >> 2) & 3);           // logical 8-column chunk of the row
+    const int64_t r = (slab / kslabs) * 256 + rr;
+    const int64_t c = (slab % kslabs) * 32 + lc * 8;
+    const uint2 raw = *reinterpret_cast<const uint2*>(q + slab_offset_i8(r, c, cols));
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t word = j < 4 ? raw.x : raw.y;
+      v[j] = static_cast<float>(static_cast<int8_t>((word >> (8 * (j & 3))) & 0xffu));
+    }
+    store16<BF16>(w + o * 8, v);
+  }
+}
+
 int grid_for(int64_t work_items) {
   int64_t g = (work_items + kThreads - 1) / kThreads;
   if (g > 65536) g = 65536;
@@ -794,6 +819,11 @@ hipError_t launch_norm_mod_quant(int64_t n_rows, int d, float eps, const void* x
     case 3: norm_quant_kernel<3, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, q, qscale, n_rows, d, eps); break;
     default: norm_quant_kernel<4, kRows><<<grid, kThreads, 0, s>>>(xx, shift, scale, q, qscale, n_rows, d, eps); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_widen_int8(int64_t rows, int64_t cols, const int8_t* q, void* w, hipStream_t s) {
+  widen_int8_kernel<<<grid_for(rows * cols / 8), kThreads, 0, s>>>(q, static_cast<uint16_t*>(w), rows, cols);
   return hipGetLastError();
 }
 

@@ -356,7 +356,9 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   float csc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) csc[j] = 1.0f;
-  if constexpr ((kInt8 || kA8) && kEpi != EPI_SWIGLU) {
+  // Weight row scales: int8 codes, or int8 codes widened to bfloat16 ahead of a bf16 launch.
+  const bool wscaled = kInt8 || kA8 || p.wscale != nullptr;
+  if (kEpi != EPI_SWIGLU && wscaled) {
     const u32x4 sraw = *reinterpret_cast<const u32x4*>(p.wscale + col_base + lc);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   if constexpr (kEpi == EPI_SWIGLU) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) { sg[j] = 1.0f; su[j] = 1.0f; }
-    if constexpr (kInt8 || kA8) {
+    if (wscaled) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(p.wscale + col_base + gcol);
       const u32x4 b = *reinterpret_cast<const u32x4*>(p.wscale + col_base + ucol);
 #pragma unroll
@@ -584,7 +586,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
           const int c = lane + 64 * half;
           const int64_t f = col_base + c - 2 * d;
           float sc = 1.0f;
-          if constexpr (kInt8 || kA8) sc = bf16_bits_to_f32(p.wscale[col_base + c]);
+          if (wscaled) sc = bf16_bits_to_f32(p.wscale[col_base + c]);
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             u32x4 out;

@@ -32,6 +32,9 @@ hipError_t launch_pack(int wdtype, int kind, int64_t rows, int64_t cols, const v
 // slab_offset_q8 order (int8 weights and int8 activations).
 hipError_t launch_pack_int8(int kind, int64_t rows, int64_t cols, const void* w_bf16,
                             int8_t* q, uint16_t* scale, int slab64, hipStream_t s);
+// int8 weight codes (slab_offset_i8 order) widened to bfloat16 in slab_offset order, exact; the
+// bf16 GEMM then multiplies them and applies the row scales given in GemmArgs.wscale.
+hipError_t launch_widen_int8(int64_t rows, int64_t cols, const int8_t* q, void* w, hipStream_t s);
 // Per-row int8 quantisation of bfloat16 rows (row-major [n_rows x cols]): codes q in
 // slab_offset_q8 order, float32 scales qscale[n_rows]. cols % 64 == 0, cols <= 32768.
 hipError_t launch_quant_rows(int64_t n_rows, int64_t cols, const void* a, int8_t* q, float* qscale,
