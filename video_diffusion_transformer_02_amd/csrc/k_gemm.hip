@@ -378,10 +378,9 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int64_t row = row_base + mb * 32 + it * kRowsPass + lr;
-      if constexpr (kEpi == EPI_RESID) {
-        xbuf[mb & 1][it] = u32x4{0u, 0u, 0u, 0u};
-        if (row < p.m)
-          xbuf[mb & 1][it] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.x) + row * p.n + col_base + lc);
+      if constexpr (kEpi == EPI_RESID) {  // rows past m read row m-1 (never stored): no branch
+        const int64_t rl = row < p.m ? row : p.m - 1;
+        xbuf[mb & 1][it] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.x) + rl * p.n + col_base + lc);
       }
       if constexpr (kA8 && kEpi != EPI_SWIGLU) rbuf[mb & 1][it] = p.ascale[row];
     }
@@ -397,23 +396,23 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   }
   if constexpr (kEpi == EPI_RESID || (kA8 && kEpi != EPI_SWIGLU)) fetch_rows(0);
   // QKV, q and k columns: a lane's 8 features lie in one RoPE chunk (axis, first pair k0); the
-  // table offsets of its rows are read once, the (cos, sin) entries one slice ahead.
+  // table offsets of its rows are read once, the (cos, sin) entries of a slice while it is staged.
   const int region = kEpi == EPI_QKV ? static_cast<int>(n0 / p.d_model) : 0;  // 0 q, 1 k, 2 v
   const int64_t fq = col_base + lc - static_cast<int64_t>(region) * p.d_model;  // first of 8 features
   [[maybe_unused]] int rbase[4][kIt];
-  [[maybe_unused]] f32x4 csb[2][kIt][2];
+  [[maybe_unused]] f32x4 csb[kIt][2];
+  // Rows past the video rows read the entries of the last video row and do not use them, so
+  // that no load sits behind a branch (a branch makes the compiler wait for every load).
+  const bool has_rope = kEpi == EPI_QKV && region < 2 && p.geom.n_video > 0;
   auto fetch_rope = [&](int mb) {
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
-      const int64_t row = row_base + mb * 32 + it * kRowsPass + lr;
-      if (row < p.geom.n_video) {
-        csb[mb & 1][it][0] = *reinterpret_cast<const f32x4*>(p.rope.table + rbase[mb][it]);
-        csb[mb & 1][it][1] = *reinterpret_cast<const f32x4*>(p.rope.table + rbase[mb][it] + 2);
-      }
+      csb[it][0] = *reinterpret_cast<const f32x4*>(p.rope.table + rbase[mb][it]);
+      csb[it][1] = *reinterpret_cast<const f32x4*>(p.rope.table + rbase[mb][it] + 2);
     }
   };
   if constexpr (kEpi == EPI_QKV) {
-    if (region < 2) {
+    if (has_rope) {
       const int dh = static_cast<int>(fq % p.rope.head_dim);
       const int ct = p.rope.head_dim / 4, cy = 3 * p.rope.head_dim / 8;
       const int axis = dh < ct ? 0 : (dh < ct + cy ? 1 : 2);
@@ -423,10 +422,16 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
 #pragma unroll
         for (int it = 0; it < kIt; ++it) {
           const int64_t row = row_base + mb * 32 + it * kRowsPass + lr;
-          rbase[mb][it] = row < p.geom.n_video ? reinterpret_cast<const int*>(p.rope.rowbase + row)[axis] + k0 : 0;
+          const int64_t rl = row < p.geom.n_video ? row : p.geom.n_video - 1;
+          rbase[mb][it] = reinterpret_cast<const int*>(p.rope.rowbase + rl)[axis] + k0;
         }
-      fetch_rope(0);
     }
+  }
+  // Transposed v (W8A8): the row scales of each slice, lane l holding row l % 32's.
+  [[maybe_unused]] float rsv[4];
+  if constexpr (kEpi == EPI_QKV && kA8) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) rsv[mb] = p.ascale[row_base + mb * 32 + li];
   }
   // SwiGLU: SN packed columns = SN/64 groups of [32 gate | 32 up] -> SN/2 h features per row;
   // a lane owns 8 consecutive features (their gate and up columns) on kItH rows per slice.
@@ -454,12 +459,15 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
     }
   }
 
+  // Tiles that lie wholly inside the m rows (all but the last row of tiles) run without per-row
+  // checks.
+  auto epilogue = [&]<bool kRagged>() {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     if constexpr (kEpi == EPI_RESID || (kA8 && kEpi != EPI_SWIGLU))
       if (mb + 1 < 4) fetch_rows(mb + 1);
-    if constexpr (kEpi == EPI_QKV)
-      if (region < 2 && mb + 1 < 4) fetch_rope(mb + 1);
+    if constexpr (kEpi == EPI_QKV)  // this slice's entries, loaded while the slice is staged
+      if (has_rope) fetch_rope(mb);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] *= rs;
         }
-        if (row < p.m) {
+        if (!kRagged || row < p.m) {
           if constexpr (kEpi == EPI_F32) {
             float* o = p.out + row * p.n + col_base + lc;
             *reinterpret_cast<f32x4*>(o) = f32x4{v[0] * csc[0], v[1] * csc[1], v[2] * csc[2], v[3] * csc[3]};
@@ -521,7 +529,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
 #pragma unroll
           for (int j = 0; j < 8; ++j) { gv[j] *= rs; uv[j] *= rs; }
         }
-        if (row < p.m) {
+        if (!kRagged || row < p.m) {
           u32x4 out;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -554,28 +562,31 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] *= rs;
           }
-          if (row < p.geom.n_video) {
-            const f32x4 cs01 = csb[mb & 1][it][0];
-            const f32x4 cs23 = csb[mb & 1][it][1];
+          if (has_rope) {
+            const bool rot = row < p.geom.n_video;  // selected, not branched on
+            const f32x4 cs01 = csb[it][0];
+            const f32x4 cs23 = csb[it][1];
             const float c[4] = {cs01[0], cs01[2], cs23[0], cs23[2]};
             const float sn[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float a = v[2 * j], b = v[2 * j + 1];
-              v[2 * j] = fmaf(a, c[j], -b * sn[j]);
-              v[2 * j + 1] = fmaf(a, sn[j], b * c[j]);
+              const float ra = fmaf(a, c[j], -b * sn[j]);
+              const float rb = fmaf(a, sn[j], b * c[j]);
+              v[2 * j] = rot ? ra : a;
+              v[2 * j + 1] = rot ? rb : b;
             }
           }
-          if (row < p.m_pad) {
-            u32x4 out;
+          // Every row of the tile is below m_pad (a multiple of 256); rows past m get zeros.
+          u32x4 out;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float y0 = row < p.m ? v[2 * j] : 0.f, y1 = row < p.m ? v[2 * j + 1] : 0.f;
-              out[j] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
-                       (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
-            }
-            *reinterpret_cast<u32x4*>(dst + row * d + f) = out;
+          for (int j = 0; j < 4; ++j) {
+            const bool live = !kRagged || row < p.m;
+            const float y0 = live ? v[2 * j] : 0.f, y1 = live ? v[2 * j + 1] : 0.f;
+            out[j] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
+                     (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
           }
+          *reinterpret_cast<u32x4*>(dst + row * d + f) = out;
         }
       } else {
         // v transposed: each lane walks one column (feature) down the 32 staged rows and writes
@@ -595,11 +606,12 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
               const int r = q4 * 8 + 2 * j;
               float s0 = sc, s1 = sc;
               if constexpr (kA8) {
-                s0 *= p.ascale[r0 + r];
-                s1 *= p.ascale[r0 + r + 1];
+                s0 *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv[mb]), r));
+                s1 *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv[mb]), r + 1));
               }
-              const float y0 = r0 + r < p.m ? st[r * kStride + c] * s0 : 0.f;
-              const float y1 = r0 + r + 1 < p.m ? st[(r + 1) * kStride + c] * s1 : 0.f;
+              const float a0 = st[r * kStride + c], a1 = st[(r + 1) * kStride + c];
+              const float y0 = (!kRagged || r0 + r < p.m) ? a0 * s0 : 0.f;
+              const float y1 = (!kRagged || r0 + r + 1 < p.m) ? a1 * s1 : 0.f;
               out[j] = static_cast<uint32_t>(f32_to_bf16_bits(y0)) |
                        (static_cast<uint32_t>(f32_to_bf16_bits(y1)) << 16);
             }
@@ -609,6 +621,9 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
       }
     }
   }
+  };
+  if (m0 + BM <= p.m) epilogue.template operator()<false>();
+  else epilogue.template operator()<true>();
 }
 
 // ---------------------------------------------------------------- float32 kernel
