@@ -184,7 +184,9 @@ h3x_status h3x_pack_int8_weights(const h3x_block_cfg *cfg, int32_t kind, const v
  * (2k, 2k+1) of a chunk of size D turns by pos * theta^(-2k/D); merged tokens sit at x = 2m+0.5;
  * audio and text rows are not turned. mod (dev [6 x d] float32): shift1, scale1, gate1,
  * shift2, scale2, gate2. ws (dev) must hold h3x_block_workspace_bytes(cfg, geom) bytes; its
- * contents on entry are ignored and on return undefined. */
+ * contents on entry are ignored and on return undefined. (With H3X_I8 weights the workspace
+ * also receives each weight matrix widened to bfloat16 just before its product: the codes are
+ * small integers, so the widening is exact and the scales are applied afterwards.) */
 size_t h3x_block_workspace_bytes(const h3x_block_cfg *cfg, const h3x_geom *geom);
 h3x_status h3x_dit_block_forward(const h3x_block_cfg *cfg, const h3x_geom *geom,
                                  const h3x_block_weights *w, const float *mod, void *x,
