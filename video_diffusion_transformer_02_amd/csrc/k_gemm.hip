@@ -372,7 +372,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   // once.
   constexpr int kIt = 32 / kRowsPass;
   [[maybe_unused]] u32x4 xbuf[2][kIt];
-  [[maybe_unused]] float rbuf[2][kIt];
+  [[maybe_unused]] float rsl[4];  // W8A8 row scales of each slice: lane l holds row l % 32's
   [[maybe_unused]] float gsc[8];
   auto fetch_rows = [&](int mb) {
 #pragma unroll
@@ -382,9 +382,14 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
         const int64_t rl = row < p.m ? row : p.m - 1;
         xbuf[mb & 1][it] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.x) + rl * p.n + col_base + lc);
       }
-      if constexpr (kA8 && kEpi != EPI_SWIGLU) rbuf[mb & 1][it] = p.ascale[row];
     }
   };
+  if constexpr (kA8 && kEpi != EPI_SWIGLU) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) rsl[mb] = p.ascale[row_base + mb * 32 + li];
+  }
+  // The row scale of row r of slice mb, for this lane.
+  auto row_scale = [&](int mb, int r) { return __shfl(rsl[mb], r, 64); };
   if constexpr (kEpi == EPI_RESID) {
     const f32x4 g0 = *reinterpret_cast<const f32x4*>(p.gate + col_base + lc);
     const f32x4 g1 = *reinterpret_cast<const f32x4*>(p.gate + col_base + lc + 4);
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
       gsc[4 + j] = g1[j] * csc[4 + j];
     }
   }
-  if constexpr (kEpi == EPI_RESID || (kA8 && kEpi != EPI_SWIGLU)) fetch_rows(0);
+  if constexpr (kEpi == EPI_RESID) fetch_rows(0);
   // QKV, q and k columns: a lane's 8 features lie in one RoPE chunk (axis, first pair k0); the
   // table offsets of its rows are read once, the (cos, sin) entries of a slice while it is staged.
   const int region = kEpi == EPI_QKV ? static_cast<int>(n0 / p.d_model) : 0;  // 0 q, 1 k, 2 v
@@ -427,12 +432,6 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
         }
     }
   }
-  // Transposed v (W8A8): the row scales of each slice, lane l holding row l % 32's.
-  [[maybe_unused]] float rsv[4];
-  if constexpr (kEpi == EPI_QKV && kA8) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) rsv[mb] = p.ascale[row_base + mb * 32 + li];
-  }
   // SwiGLU: SN packed columns = SN/64 groups of [32 gate | 32 up] -> SN/2 h features per row;
   // a lane owns 8 consecutive features (their gate and up columns) on kItH rows per slice.
   constexpr int kLanesH = SN / 16, kRowsH = 64 / kLanesH, kItH = 32 / kRowsH;
@@ -464,7 +463,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
   auto epilogue = [&]<bool kRagged>() {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    if constexpr (kEpi == EPI_RESID || (kA8 && kEpi != EPI_SWIGLU))
+    if constexpr (kEpi == EPI_RESID)
       if (mb + 1 < 4) fetch_rows(mb + 1);
     if constexpr (kEpi == EPI_QKV)  // this slice's entries, loaded while the slice is staged
       if (has_rope) fetch_rope(mb);
@@ -486,7 +485,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + r * kStride + lc + 4);
         float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         if constexpr (kA8) {
-          const float rs = rbuf[mb & 1][it];
+          const float rs = row_scale(mb, r);
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] *= rs;
         }
@@ -558,7 +557,7 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
           float v[8] = {v0[0] * csc[0], v0[1] * csc[1], v0[2] * csc[2], v0[3] * csc[3],
                         v1[0] * csc[4], v1[1] * csc[5], v1[2] * csc[6], v1[3] * csc[7]};
           if constexpr (kA8) {
-            const float rs = rbuf[mb & 1][it];
+            const float rs = row_scale(mb, r);
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] *= rs;
           }
@@ -606,8 +605,8 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
               const int r = q4 * 8 + 2 * j;
               float s0 = sc, s1 = sc;
               if constexpr (kA8) {
-                s0 *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv[mb]), r));
-                s1 *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsv[mb]), r + 1));
+                s0 *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsl[mb]), r));
+                s1 *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rsl[mb]), r + 1));
               }
               const float a0 = st[r * kStride + c], a1 = st[(r + 1) * kStride + c];
               const float y0 = (!kRagged || r0 + r < p.m) ? a0 * s0 : 0.f;
