@@ -163,11 +163,10 @@ def test_attention(B, wl, tol, n, sharp):
 @pytest.mark.parametrize("slots", [16, 12, 5, 100, 0])
 def test_attention_work_split(B, record, slots):
     """The work plan for `slots` resident workgroups, for 1000 tokens and 4 heads (16 items of
-    256 queries with the eight-wave kernel, 32 of 128 with the four-wave one; 16 key tiles):
-    16 runs every item whole; 12 and 5 leave a last round of 4 and 1 items cut into 3 and 4
-    key pieces (eight waves; four waves: whole, and 2 items in 2 pieces); 100 and the device's
-    default cut every item (6 or 3 pieces, or one tile each). Every plan agrees with the
-    oracle, and with the plan for one slot (never split) up to the merge's rounding."""
+    256 queries, 16 key tiles): 16 runs every item whole; 12 and 5 leave a last round of 4 and
+    1 items cut into 3 and 4 key pieces; 100 and the device's default cut every item (6 pieces,
+    or one tile each). Every plan agrees with the oracle, and with the plan for one slot (never
+    split) up to the merge's rounding."""
     wl = SMALL
     cfg = binding_cfg(wl)
     n, d = 1000, wl.d_model

@@ -1,11 +1,10 @@
 // Full bidirectional attention over the joint token sequence, softmax(q k^T / sqrt(Dh)) v per
 // head, with no mask (every token attends to every token).
 //
-//  * attn_mfma8_kernel / attn_mfma_kernel (bfloat16, Dh = 128): flash attention with online
-//    softmax. A workgroup of eight (default) or four waves owns 256 or 128 queries of one head
-//    (32 per wave) and walks the keys in tiles of 64, double-buffered in LDS and fetched by
-//    buffer loads that write LDS directly; the eight-wave form shares each tile between twice
-//    the queries, halving the tile traffic into LDS and through L2. Each wave
+//  * attn_mfma8_kernel (bfloat16, Dh = 128): flash attention with online softmax. A workgroup
+//    of eight waves (one per CU, two per SIMD) owns 256 queries of one head (32 per wave) and
+//    walks the keys in tiles of 64, double-buffered in LDS and fetched by buffer loads that
+//    write LDS directly; each tile is shared by all 256 queries. Each wave
 //    computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that a lane holds 32 scores of a
 //    single query: a max needs one cross-lane exchange (lane ^ 32), the running sum none until
 //    the end. The probabilities are already in the B-operand layout of O^T += V^T P^T, so they
@@ -19,8 +18,6 @@
 //  * attn_f32_kernel: float32, one thread per (query, head), online softmax over keys; the
 //    k and v reads of a wave are broadcasts (all its lanes read the same key).
 #include <math.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include "launch.h"
 
@@ -149,17 +146,16 @@ __device__ __forceinline__ void attn_body(const uint16_t* __restrict__ q, const 
     const uint8_t* sv = smem + kVBase + kStage * kTile;
 
     // S^T: sacc[kh] element 4b + r holds key 32kh + 16(b >> 1) + 8hi + 4(b & 1) + r of the tile.
+    // The two 32-key halves alternate, so no MFMA waits on the one just issued.
     const f32x16 zero = {};
-    f32x16 sacc[2];
+    f32x16 sacc[2] = {zero, zero};
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      sacc[kh] = zero;
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int kh = 0; kh < 2; ++kh) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(sk + kh * 8192 + k_rd[s]));
         sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kh], 0, 0, 0);
       }
-    }
     if constexpr (kTail) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
@@ -283,14 +279,6 @@ __device__ __forceinline__ void attn_body(const uint16_t* __restrict__ q, const 
   }
 }
 
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
-                                                           const uint16_t* __restrict__ k,
-                                                           const uint16_t* __restrict__ vt,
-                                                           uint16_t* __restrict__ o, int n, int n_pad,
-                                                           int n_heads, AttnPlan plan, int full_grid,
-                                                           int o_tiled, float* __restrict__ part) {
-  attn_body<4>(q, k, vt, o, n, n_pad, n_heads, plan, full_grid, o_tiled, part);
-}
 __global__ __launch_bounds__(512, 1) void attn_mfma8_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ vt,
@@ -382,21 +370,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   }
 }
 
-// Workgroup size of the bfloat16 kernel: eight waves (256 queries sharing each K/V tile, one
-// workgroup per CU; the default), or four (128 queries, two workgroups per CU) with
-// H3X_ATTN_MODE=w4.
-int attn_waves() {
-  static const int w = [] {
-    const char* e = getenv("H3X_ATTN_MODE");
-    return (e && strcmp(e, "w4") == 0) ? 4 : 8;
-  }();
-  return w;
-}
-
 }  // namespace
 
 int attention_slots(int requested) {
-  const int cap = kAttnMaxPieceQueries / (32 * attn_waves());
+  const int cap = kAttnMaxPieceQueries / kAttnQueries;
   if (requested > 0) return requested < cap ? requested : cap;
   static int cached[64] = {0};
   int dev = 0;
@@ -406,15 +383,14 @@ int attention_slots(int requested) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     cached[dev] = cus;
   }
-  // Two waves per SIMD: two four-wave workgroups or one eight-wave workgroup per CU.
-  const int per_cu = 8 / attn_waves();
-  return per_cu * cached[dev] < cap ? per_cu * cached[dev] : cap;
+  // One eight-wave workgroup per CU (two waves per SIMD).
+  return cached[dev] < cap ? cached[dev] : cap;
 }
 
 AttnPlan attention_plan(int64_t n_tokens, int n_heads, int slots) {
   AttnPlan p;
   const int n = static_cast<int>(n_tokens);
-  p.bq = 32 * attn_waves();
+  p.bq = kAttnQueries;
   p.qblocks = (n + p.bq - 1) / p.bq;
   p.items = p.qblocks * n_heads;
   p.ktiles = (n + kBK - 1) / kBK;
@@ -453,17 +429,11 @@ hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_head
     const uint16_t* vv = static_cast<const uint16_t*>(vt);
     uint16_t* oo = static_cast<uint16_t*>(o);
     float* pp = static_cast<float*>(ws);
-    if (plan.bq == 256)
-      attn_mfma8_kernel<<<grid, 512, 0, s>>>(qq, kk, vv, oo, n, np, n_heads, plan, full_grid, o_tiled, pp);
-    else
-      attn_mfma_kernel<<<grid, 256, 0, s>>>(qq, kk, vv, oo, n, np, n_heads, plan, full_grid, o_tiled, pp);
+    attn_mfma8_kernel<<<grid, 512, 0, s>>>(qq, kk, vv, oo, n, np, n_heads, plan, full_grid, o_tiled, pp);
     if (plan.rem > 0) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      if (plan.bq == 256)
-        attn_combine_kernel<256><<<plan.rem * 16, 256, 0, s>>>(oo, pp, n, n_heads, plan, o_tiled);
-      else
-        attn_combine_kernel<128><<<plan.rem * 8, 256, 0, s>>>(oo, pp, n, n_heads, plan, o_tiled);
+      attn_combine_kernel<kAttnQueries><<<plan.rem * (kAttnQueries / 16), 256, 0, s>>>(oo, pp, n, n_heads, plan, o_tiled);
     }
   } else {
     dim3 grid(static_cast<unsigned>((n + 63) / 64), static_cast<unsigned>(n_heads));

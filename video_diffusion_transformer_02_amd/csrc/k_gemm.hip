@@ -4,9 +4,9 @@
 //    the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16). 256 x 256 output tile per workgroup of
 //    eight waves (2 x 4, each 128 x 64), K step 32 in a five-stage LDS pipeline filled by
 //    buffer loads that write LDS directly (operands stored as 256 x 32 slabs in LDS order, so a
-//    K step is one contiguous copy). By default the two halves of the workgroup (one wave of
-//    each per SIMD) run ping-pong: while one issues its MFMAs the other reads its next
-//    fragments and streams the next K step, offset by one barrier interval. int8 weights are
+//    K step is one contiguous copy). The two halves of the workgroup (one wave of each per
+//    SIMD) run ping-pong: while one issues its MFMAs the other reads its next fragments and
+//    streams the next K step, offset by one barrier interval. int8 weights are
 //    widened to bfloat16 in registers (exact: |q| <= 127) and their per-row scale is applied in
 //    the epilogue. W8A8 (int8 weights and per-row int8 activations): the same pipeline over
 //    64-code K steps (a 256 x 64-byte slab per operand, the byte layout of a bfloat16 step) on
@@ -20,9 +20,6 @@
 // Epilogues: QKV (3D RoPE on video rows of q and k, v written transposed, pad rows zeroed),
 // gated residual (x += gate * acc), SwiGLU over the 32-row gate/up interleave, float32 store.
 #include <math.h>
-#include <stdlib.h>
-#include <string.h>
-
 #include <type_traits>
 
 #include "launch.h"
@@ -32,10 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int BM = 256, BN = 256, BK = 32;
-#ifndef H3X_GEMM_STAGES
-#define H3X_GEMM_STAGES 5
-#endif
-constexpr int kStages = H3X_GEMM_STAGES;  // LDS stages of the K pipeline (32 KB each for bf16)
+constexpr int kStages = 5;  // LDS stages of the K pipeline (32 KB each for bf16)
 
 // ---------------------------------------------------------------- shared epilogue math
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -122,7 +116,7 @@ struct Layout {
   static constexpr int NB = SN / 32;   // 32-wide MFMA blocks per wave along N
 };
 
-template <bool kInt8, int kEpi, int kWN, bool kATiled, bool kPingPong, bool kA8>
+template <bool kInt8, int kEpi, int kWN, bool kATiled, bool kA8>
 __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(GemmArgs p, int tiles_m,
                                                                                 int tiles_n, int group_m) {
   static_assert(!kA8 || (kATiled && !kInt8), "W8A8 takes tiled int8 activations and 64-byte weight slabs");
@@ -249,96 +243,44 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
       for (int nb = 0; nb < NB; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a[mb]), bv[nb], acc[mb][nb], 0, 0, 0);
   };
-  // One LDS read between consecutive MFMAs until the next slice's fragments are all requested,
-  // then the remaining MFMAs back to back; kVmem buffer loads ride along with each pair.
-  constexpr int kReads = 4 + NB, kMfmas = 4 * NB;
-  auto interleave = [&]<int kVmem>() {
-#pragma unroll
-    for (int i = 0; i < kReads; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      if constexpr (kVmem > 0) __builtin_amdgcn_sched_group_barrier(0x020, kVmem, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kReads, 0);
-    __builtin_amdgcn_sched_barrier(0);  // nothing crosses: keeps each slice's MFMAs together
+  // Ping-pong schedule (eight waves, two per SIMD): waves 0-3 and 4-7 alternate between a
+  // memory phase (stream a future K step into LDS, read this K step's fragments) and a
+  // compute phase (its 16 MFMAs), offset by one barrier interval, so that on every SIMD one
+  // wave feeds the matrix core while the other one loads. Every interval ends with a
+  // workgroup barrier at which each wave has at most kStages-2 of its K-step loads in
+  // flight: the step read next has landed, and the stage written next has been read by both
+  // groups in earlier intervals.
+  Frags fa, fb;
+  const int group = wave / kWN;
+  auto barrier_main = [&]() { pipeline_barrier<(kStages - 2) * kLoads>(); };
+  auto barrier_drain = [&]() { pipeline_barrier<0>(); };
+  auto compute = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+    mma(fa);
+    mma(fb);
+    __builtin_amdgcn_s_setprio(0);
   };
-
-  if constexpr (kPingPong) {
-    // Ping-pong schedule (eight waves, two per SIMD): waves 0-3 and 4-7 alternate between a
-    // memory phase (stream a future K step into LDS, read this K step's fragments) and a
-    // compute phase (its 16 MFMAs), offset by one barrier interval, so that on every SIMD one
-    // wave feeds the matrix core while the other one loads. Every interval ends with a
-    // workgroup barrier at which each wave has at most kStages-2 of its K-step loads in
-    // flight: the step read next has landed, and the stage written next has been read by both
-    // groups in earlier intervals.
-    Frags fa, fb;
-    const int group = wave / kWN;
-    auto barrier_main = [&]() { pipeline_barrier<(kStages - 2) * kLoads>(); };
-    auto barrier_drain = [&]() { pipeline_barrier<0>(); };
-    auto compute = [&]() {
-      __builtin_amdgcn_s_setprio(1);
-      mma(fa);
-      mma(fb);
-      __builtin_amdgcn_s_setprio(0);
-    };
-    const int pre = ktiles < kStages - 1 ? ktiles : kStages - 1;
-    for (int t = 0; t < pre; ++t) issue_loads(t);
-    if (pre == kStages - 1) barrier_main(); else barrier_drain();
-    if (group == 1) barrier_main();  // group 1 runs one interval behind
-    int kt = 0;
-    for (; kt + kStages - 1 < ktiles; ++kt) {
-      read_frags(kt, 0, fa);
-      read_frags(kt, 1, fb);
-      issue_loads(kt + kStages - 1);
-      barrier_main();
-      compute();
-      barrier_main();
-    }
-    for (; kt < ktiles; ++kt) {
-      read_frags(kt, 0, fa);
-      read_frags(kt, 1, fb);
-      barrier_drain();
-      compute();
-      barrier_drain();
-    }
-    if (group == 0) barrier_drain();  // same number of barriers in both groups
-  } else {
-    // kStages LDS stages, K step 32 (two 16-wide slices), one barrier per K step. K step
-    // kt+kStages-1 streams into the stage that K step kt-1 left while kt is multiplied; the
-    // fragments of the next slice are read while the current one is multiplied. kAhead = K steps
-    // in flight beyond kt+1 (kStages-2 in steady state), so waiting for vmcnt <= kAhead * kLoads
-    // leaves step kt+1 landed.
-    Frags f0, f1;
-    auto k_step = [&]<int kAhead>(int kt) {
-      read_frags(kt, 1, f1);
-      if constexpr (kAhead == kStages - 2) issue_loads(kt + kStages - 1);
-      mma(f0);
-      interleave.template operator()<kAhead == kStages - 2 ? (kLoads + kReads - 1) / kReads : 0>();
-      pipeline_barrier<(kAhead > 0 ? kAhead : 0) * kLoads>();
-      if constexpr (kAhead >= 0) read_frags(kt + 1, 0, f0);
-      mma(f1);
-      interleave.template operator()<0>();
-    };
-    // Prologue: K steps 0 .. kStages-2 in flight, wait for step 0.
-    const int pre = ktiles < kStages - 1 ? ktiles : kStages - 1;
-    for (int t = 0; t < pre; ++t) issue_loads(t);
-    switch (pre) {
-      case 5: pipeline_barrier<4 * kLoads>(); break;
-      case 4: pipeline_barrier<3 * kLoads>(); break;
-      case 3: pipeline_barrier<2 * kLoads>(); break;
-      case 2: pipeline_barrier<kLoads>(); break;
-      default: pipeline_barrier<0>(); break;
-    }
-    read_frags(0, 0, f0);
-    int kt = 0;
-    for (; kt + kStages - 1 < ktiles; ++kt) k_step.template operator()<kStages - 2>(kt);
-    // Drain: fewer and fewer K steps remain in flight.
-    if constexpr (kStages - 3 >= 3) if (kt + 4 < ktiles) k_step.template operator()<3>(kt++);
-    if constexpr (kStages - 3 >= 2) if (kt + 3 < ktiles) k_step.template operator()<2>(kt++);
-    if constexpr (kStages - 3 >= 1) if (kt + 2 < ktiles) k_step.template operator()<1>(kt++);
-    if (kt + 1 < ktiles) k_step.template operator()<0>(kt++);
-    k_step.template operator()<-1>(kt);
+  const int pre = ktiles < kStages - 1 ? ktiles : kStages - 1;
+  for (int t = 0; t < pre; ++t) issue_loads(t);
+  if (pre == kStages - 1) barrier_main(); else barrier_drain();
+  if (group == 1) barrier_main();  // group 1 runs one interval behind
+  int kt = 0;
+  for (; kt + kStages - 1 < ktiles; ++kt) {
+    read_frags(kt, 0, fa);
+    read_frags(kt, 1, fb);
+    issue_loads(kt + kStages - 1);
+    barrier_main();
+    compute();
+    barrier_main();
   }
+  for (; kt < ktiles; ++kt) {
+    read_frags(kt, 0, fa);
+    read_frags(kt, 1, fb);
+    barrier_drain();
+    compute();
+    barrier_drain();
+  }
+  if (group == 0) barrier_drain();  // same number of barriers in both groups
 
   // ---- epilogue through LDS. Each wave stages its 128 x SN float32 result 32 rows at a time
   // (row stride SN + 8 floats: the two half-waves of an MFMA block store to disjoint banks),
@@ -708,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs p) {
   }
 }
 
-template <bool kInt8, int kWN, bool kATiled, bool kPP, bool kA8 = false>
+template <bool kInt8, int kWN, bool kATiled, bool kA8 = false>
 hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   const int tiles_m = static_cast<int>((a.m + BM - 1) / BM);
   const int tiles_n = static_cast<int>(a.n / BN);
@@ -718,35 +660,19 @@ hipError_t launch_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   constexpr int T = Layout<kWN>::kThreadsT;
   switch (epi) {
     case EPI_QKV:
-      gemm_mfma_kernel<kInt8, EPI_QKV, kWN, kATiled, kPP, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_QKV, kWN, kATiled, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_RESID:
-      gemm_mfma_kernel<kInt8, EPI_RESID, kWN, kATiled, kPP, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_RESID, kWN, kATiled, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     case EPI_SWIGLU:
-      gemm_mfma_kernel<kInt8, EPI_SWIGLU, kWN, kATiled, kPP, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_SWIGLU, kWN, kATiled, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
     default:
-      gemm_mfma_kernel<kInt8, EPI_F32, kWN, kATiled, kPP, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
+      gemm_mfma_kernel<kInt8, EPI_F32, kWN, kATiled, kA8><<<grid, T, 0, s>>>(a, tiles_m, tiles_n, group_m);
       break;
   }
   return hipGetLastError();
-}
-
-// Schedule of the MFMA GEMM: eight waves (128 x 64 each) in ping-pong (the default), or in step
-// (H3X_GEMM_MODE=w8).
-int gemm_mode_pp() {
-  static const int m = [] {
-    const char* e = getenv("H3X_GEMM_MODE");
-    return (e && strcmp(e, "w8") == 0) ? 0 : 1;
-  }();
-  return m;
-}
-
-template <bool kInt8, bool kATiled>
-hipError_t launch_mode(int epi, const GemmArgs& a, hipStream_t s) {
-  if (gemm_mode_pp()) return launch_mfma<kInt8, 4, kATiled, true>(epi, a, s);
-  return launch_mfma<kInt8, 4, kATiled, false>(epi, a, s);
 }
 
 }  // namespace
@@ -765,13 +691,10 @@ hipError_t launch_gemm(int act, int wdtype, int epi, const GemmArgs& a, hipStrea
     }
     return hipGetLastError();
   }
-  if (wdtype == H3X_I8A8) {
-    if (gemm_mode_pp()) return launch_mfma<false, 4, true, true, true>(epi, a, s);
-    return launch_mfma<false, 4, true, false, true>(epi, a, s);
-  }
+  if (wdtype == H3X_I8A8) return launch_mfma<false, 4, true, true>(epi, a, s);
   const bool i8 = wdtype == H3X_I8;
-  if (a.a_tiled) return i8 ? launch_mode<true, true>(epi, a, s) : launch_mode<false, true>(epi, a, s);
-  return i8 ? launch_mode<true, false>(epi, a, s) : launch_mode<false, false>(epi, a, s);
+  if (a.a_tiled) return i8 ? launch_mfma<true, 4, true>(epi, a, s) : launch_mfma<false, 4, true>(epi, a, s);
+  return i8 ? launch_mfma<true, 4, false>(epi, a, s) : launch_mfma<false, 4, false>(epi, a, s);
 }
 
 }  // namespace h3x

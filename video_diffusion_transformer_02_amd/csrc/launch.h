@@ -121,6 +121,7 @@ struct AttnPlan {
 };
 // Partial results of at most 2^17 queries (pieces x bq) are kept: O (fp32, 128 dims), max, sum.
 constexpr int kAttnMaxPieceQueries = 1 << 17;
+constexpr int kAttnQueries = 256;  // queries per workgroup of the bfloat16 attention (8 waves x 32)
 constexpr size_t attn_part_bytes(int bq) { return static_cast<size_t>(bq) * (128 * 4 + 2 * 4); }
 int attention_slots(int requested);  // 0 = what the current device runs at once
 AttnPlan attention_plan(int64_t n_tokens, int n_heads, int slots);
