@@ -1,6 +1,6 @@
 """Full-size checks in the benchmark's launch configuration: the 45-block schedules at 6 x 32 x 32
 + 256 + 512 tokens (with and without token reduction over blocks 10..34) and the 50-block
-int8-weight schedule at 6 x 30 x 54 + 256 + 512 tokens.
+int8-weight (W8A16 and W8A8) schedules at 6 x 30 x 54 + 256 + 512 tokens.
 
 The oracle cannot run 45 full-size blocks, so two kinds of check are used:
 * a property that holds at any size: with every gate zero each block is the identity, so a
@@ -48,7 +48,10 @@ def _gpu_blocks(B, wl, cfg, seed0):
     return packed
 
 
-@pytest.mark.parametrize("wl", [synth.DENOISE45, synth.DENOISE45_TR, synth.INT8_50], ids=lambda w: w.name)
+W8A8_50 = synth.INT8_50.replace(name="w8a8_50blk_4step_6x30x54", weight="i8a8")
+
+
+@pytest.mark.parametrize("wl", [synth.DENOISE45, synth.DENOISE45_TR, synth.INT8_50, W8A8_50], ids=lambda w: w.name)
 def test_full_size_identity_step_is_bit_exact(B, wl):
     cfg, g, og = binding_cfg(wl), binding_geom(wl), oracle_geom(wl)
     packed = _gpu_blocks(B, wl, cfg, 7000)
