@@ -39,8 +39,8 @@ h3x_status h3x_qkv_project(const h3x_block_cfg *cfg, const h3x_geom *geom, const
                            void *q, void *k, void *vt, void *stream);
 
 /* o (dev [N x d] act type) = per-head softmax(q k^T / sqrt(Dh)) v over all N keys.
- * bfloat16: the work (128 queries of one head per workgroup) is planned for `slots` workgroups
- * running at once (0 = two per compute unit of the current device, at most 1024); the queries
+ * bfloat16: the work (256 queries of one head per workgroup) is planned for `slots` workgroups
+ * running at once (0 = one per compute unit of the current device, at most 512); the queries
  * of a last, partly filled round are split over key ranges whose partial results go to ws (dev,
  * h3x_attention_workspace_bytes for the same arguments, 0 when nothing is split) and are merged
  * by a second kernel. float32 needs no workspace. */
