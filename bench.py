@@ -6,7 +6,9 @@ Default run (one GPU):
     SwiGLU inner 24576, 6 x 32 x 32 video + 256 audio + 512 text tokens, bf16 weights and
     activations with float32 accumulation. `value` = algorithmic block FLOPs / time (TFLOP/s).
   * roofline of the dominant kernel (the gate/up + SwiGLU GEMM), timed with HIP events around
-    its launches on the launch stream inside the timed region.
+    its launches on the launch stream inside the timed region; also as a fraction of the
+    measured MFMA rate (mfma_probe: register-only MFMAs with changing random operands) next to
+    the device copy rate (hbm_copy_gbs).
   * cpu_baseline: the float64 NumPy oracle on a bounded sample of the same block (all K/V rows,
     a few query rows), on this host's cores.
   * block_w8a8: the same block with int8 weights and per-row int8 activations (int8 matrix
@@ -110,6 +112,23 @@ def measure_copy(B, torch, nbytes=1 << 30, reps=10):
     del src, dst
     torch.cuda.empty_cache()
     return 2.0 * nbytes / ms / 1e6
+
+
+def measure_mfma(B, torch, dtype, iters=4000, reps=3):
+    """Dense MFMA rate with register operands that change every instruction (h3x_mfma_probe):
+    the ceiling the GEMMs' instruction mix can reach at the clock the chip holds under matrix
+    work, in TFLOP/s (TOP/s for int8)."""
+    out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    B.mfma_probe(dtype, iters, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    ops = 0.0
+    for _ in range(reps):
+        ops += B.mfma_probe(dtype, iters, out)
+    e1.record()
+    torch.cuda.synchronize()
+    return ops / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 def bench_block(args, B, torch, synth, weight="bf16"):
@@ -428,6 +447,10 @@ def main():
     ms, flops, kern, roof, state = bench_block(args, B, torch, synth)
     copy_gbs = measure_copy(B, torch)
     log(f"[bench] device copy {copy_gbs:.0f} GB/s (read + write)")
+    probe = {"bf16_tflops": round(measure_mfma(B, torch, B.BF16), 1),
+             "i8_tops": round(measure_mfma(B, torch, B.I8), 1)}
+    log(f"[bench] MFMA probe {probe['bf16_tflops']:.0f} TFLOP/s bf16, {probe['i8_tops']:.0f} TOP/s int8")
+    roof["frac_of_probe"] = round(roof["achieved"] / probe["bf16_tflops"], 4)
     sampler = bench_sampler(args, B, torch, synth)
     for e in sampler.values():
         e["frac_copy"] = round(e["gbs"] / copy_gbs, 3)
@@ -437,6 +460,7 @@ def main():
     w8a8 = None
     if not args.no_w8a8:
         ms8, _, kern8, roof8, _ = bench_block(args, B, torch, synth, "i8a8")
+        roof8["frac_of_probe"] = round(roof8["achieved"] / probe["i8_tops"], 4)
         w8a8 = {"ms_per_step": round(ms8, 4), "tops": round(flops / ms8 / 1e9, 2),
                 "speedup_vs_bf16": round(ms / ms8, 3), "dominant": roof8, "kernels": kern8}
     denoise = None if args.no_denoise else bench_denoise(args, B, torch, synth)
@@ -461,6 +485,7 @@ def main():
         "frac_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
         "hbm_copy_gbs": round(copy_gbs, 1),
+        "mfma_probe": probe,
         "sampler_kernels": sampler,
         "cpu_baseline": cpu,
         "kernels": kern,

@@ -107,6 +107,15 @@ h3x_status h3x_euler(const h3x_block_cfg *cfg, int64_t n_rows, float *z, const v
  * calibrate hardware byte counters against a transfer of known size. */
 h3x_status h3x_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/* Matrix-core throughput probe: one workgroup per compute unit runs `iters` (1 .. 2^32)
+ * iterations of 64 MFMAs per wave (v_mfma_f32_32x32x16_bf16 for H3X_BF16,
+ * v_mfma_i32_32x32x32_i8 for H3X_I8) on register operands of pseudo-random values that change
+ * from one instruction to the next, with no memory traffic. *ops (host) receives the launch's
+ * operation count (2 per multiply-add); out (dev, one float) is written only to keep the
+ * products alive. Timing the call gives the rate the chip sustains for dense MFMA work at the
+ * clock it holds under that load. */
+h3x_status h3x_mfma_probe(int32_t dtype, int64_t iters, float *out, double *ops, void *stream);
+
 /* Per-kernel timing. While enabled, every launch made by the library is bracketed by HIP
  * events on its stream. h3x_profile_end waits for the recorded events, writes at most
  * max_entries per-kernel totals and returns the number written (or -1 on error). */

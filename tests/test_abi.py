@@ -234,6 +234,17 @@ def test_w8a8_kernel_level_contract(B):
     assert L.h3x_linear_a8_f32out(ctypes.byref(c), 1, 4, FAKE, None, FAKE, FAKE, FAKE, None) == 1
 
 
+def test_mfma_probe_rejects_before_launch(B):
+    L = B.lib()
+    ops = ctypes.c_double(-1.0)
+    assert L.h3x_mfma_probe(0, 10, FAKE, ctypes.byref(ops), None) == 1  # float32: no such probe
+    assert L.h3x_mfma_probe(3, 10, FAKE, ctypes.byref(ops), None) == 1
+    assert L.h3x_mfma_probe(1, 0, FAKE, ctypes.byref(ops), None) == 1
+    assert L.h3x_mfma_probe(1, 10, None, ctypes.byref(ops), None) == 1
+    assert L.h3x_mfma_probe(2, 10, FAKE, None, None) == 1
+    assert ops.value == -1.0
+
+
 def test_status_strings(B):
     L = B.lib()
     assert L.h3x_status_string(0) == b"ok"

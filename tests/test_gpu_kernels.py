@@ -274,3 +274,27 @@ def test_euler_bit_exact(B, act):
         ref = sampler.euler_update(z, sampler.sigma_delta(sigma, sigma_next), v)
         np.testing.assert_array_equal(zd.cpu().numpy().view(np.uint32), ref.view(np.uint32))
         np.testing.assert_array_equal(host(vcopy), v)
+
+
+# ---------------------------------------------------------------- measurement probe
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_mfma_probe_counts_and_runs(B, dtype):
+    """The probe's operation count is 64 MFMAs x 8 waves x one workgroup per CU per iteration,
+    and doubling the iterations takes about twice as long (the launch is MFMA work, not
+    overhead)."""
+    code = B.BF16 if dtype == "bf16" else B.I8
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    per = 2 * 32 * 32 * (16 if dtype == "bf16" else 32) * 64 * 8 * cus
+    assert B.mfma_probe(code, 7, out) == per * 7
+    times = []
+    for iters in (500, 1000):
+        B.mfma_probe(code, iters, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.mfma_probe(code, iters, out)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    assert 1.6 < times[1] / times[0] < 2.4

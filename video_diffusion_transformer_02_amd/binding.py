@@ -121,6 +121,7 @@ SIGNATURES = {
     "h3x_token_unmerge": (_I32, [_CFG, _GEOM, _P, _P, _P]),
     "h3x_euler": (_I32, [_CFG, _I64, _P, _P, _F, _F, _P, _P]),
     "h3x_copy": (_I32, [_P, _P, _SZ, _P]),
+    "h3x_mfma_probe": (_I32, [_I32, _I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "h3x_profile_begin": (_I32, []),
     "h3x_profile_end": (_I32, [ctypes.POINTER(KernelTime), _I32]),
 }
@@ -367,6 +368,13 @@ def euler(cfg, z, v, sigma, sigma_next, v_copy=None):
 
 def copy(src, dst):
     _check(lib().h3x_copy(_p(src), _p(dst), src.numel() * src.element_size(), _stream()), "copy")
+
+
+def mfma_probe(dtype, iters, out):
+    """Launch the matrix-core throughput probe (dtype BF16 or I8); returns its operation count."""
+    ops = ctypes.c_double(0.0)
+    _check(lib().h3x_mfma_probe(dtype, iters, _p(out), ctypes.byref(ops), _stream()), "mfma_probe")
+    return ops.value
 
 
 def profile_begin():

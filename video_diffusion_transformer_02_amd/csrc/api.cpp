@@ -875,6 +875,16 @@ h3x_status h3x_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return H3X_OK;
 }
 
+h3x_status h3x_mfma_probe(int32_t dtype, int64_t iters, float* out, double* ops, void* stream) {
+  if (dtype != H3X_BF16 && dtype != H3X_I8) return fail(H3X_EINVAL, "mfma_probe: dtype must be H3X_BF16 or H3X_I8");
+  if (iters < 1 || iters > (int64_t(1) << 32)) return fail(H3X_EINVAL, "mfma_probe: iters out of range");
+  if (!out || !ops) return fail(H3X_EINVAL, "mfma_probe: NULL pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  *ops = mfma_probe_ops(dtype == H3X_I8, iters);
+  H3X_LAUNCH("mfma_probe", s, launch_mfma_probe(dtype == H3X_I8, iters, out, s));
+  return H3X_OK;
+}
+
 h3x_status h3x_profile_begin(void) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = true;

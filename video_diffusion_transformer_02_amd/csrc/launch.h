@@ -24,6 +24,10 @@ hipError_t launch_core(int act, int op, int64_t n_elems, void* x, float* delta, 
 hipError_t launch_assemble(int act, int64_t n_state, int64_t n_text, int d, const float* z,
                            const void* text, void* x, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// Matrix-core throughput probe (k_probe.hip): i8 selects v_mfma_i32_32x32x32_i8, else
+// v_mfma_f32_32x32x16_bf16; mfma_probe_ops = operations (2 per multiply-add) of one launch.
+hipError_t launch_mfma_probe(int i8, int64_t iters, float* out, hipStream_t s);
+double mfma_probe_ops(int i8, int64_t iters);
 hipError_t launch_rope_table(const GeomDev& g, int head_dim, float theta, float2* table,
                              int4* rowbase, hipStream_t s);
 hipError_t launch_pack(int wdtype, int kind, int64_t rows, int64_t cols, const void* w,
