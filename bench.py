@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--block-weight", default="bf16", choices=["bf16", "i8", "i8a8"],
                    help="weight type of the block timed with --only-block")
     p.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 block and schedule")
+    p.add_argument("--only-probe", action="store_true",
+                   help="the MFMA throughput probe alone, bf16 then int8 (for profilers)")
     p.add_argument("--only-sampler", action="store_true",
                    help="the memory-bound kernels alone at the block shape (for profilers)")
     p.add_argument("--copy-calib", action="store_true",
@@ -437,6 +439,11 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     B.lib()
+    if args.only_probe:
+        probe = {"bf16_tflops": round(measure_mfma(B, torch, B.BF16), 1),
+                 "i8_tops": round(measure_mfma(B, torch, B.I8), 1)}
+        print(json.dumps({"mfma_probe": probe}))
+        return
     if args.only_sampler:
         print(json.dumps({"sampler_kernels": bench_sampler(args, B, torch, synth)}))
         return
