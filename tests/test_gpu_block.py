@@ -14,6 +14,11 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 1e-2, "i8": 2e-2}
 # Larger weights make the residual branches as large as the stream and the attention sharp.
 STRONG = SMALL.replace(name="small_bf16_strong", w_std=0.1, qkv_std=0.1, seed_base=14)
+# Another shape: d 1536 (12 heads), F 4608, 2 x 16 x 20 video + 64 audio + 77 text = 781 tokens
+# (4 row tiles, the last with 13 rows; 18 QKV and 36 gate/up column tiles; 13 key tiles).
+MID = SMALL.replace(name="mid_bf16", d_model=1536, n_heads=12, ffn_inner=4608, frames=2, grid_h=16,
+                    grid_w=20, n_audio=64, n_text=77, seed_base=16)
+MID_I8 = MID.replace(name="mid_i8", weight="i8", seed_base=17)
 
 
 @pytest.fixture(scope="module")
@@ -56,7 +61,7 @@ def run_block(B, wl, x, b=0, merged=False, mod=None, poison=False):
 
 
 
-@pytest.mark.parametrize("wl", [synth.TINY, synth.TINY_SHARP, SMALL, SMALL_F32, SMALL_I8, STRONG],
+@pytest.mark.parametrize("wl", [synth.TINY, synth.TINY_SHARP, SMALL, SMALL_F32, SMALL_I8, STRONG, MID, MID_I8],
                          ids=lambda w: w.name)
 @pytest.mark.parametrize("merged", [False, True])
 def test_block_all_rows(B, wl, merged, record):

@@ -10,12 +10,13 @@ from oracle import dit, quant, sampler
 from oracle.numeric import bf16_rne, round_storage
 from _util import (binding_cfg, binding_geom, host, modulation, oracle_geom, packed_block, rel_l2,
                    to_dev, unslab)
-from test_gpu_block import branch_bound
+from test_gpu_block import MID, branch_bound
 from test_gpu_kernels import SMALL, _src
 
 pytestmark = pytest.mark.gpu
 
 SMALL_A8 = SMALL.replace(name="small_i8a8", weight="i8a8", seed_base=15)
+MID_A8 = MID.replace(name="mid_i8a8", weight="i8a8", seed_base=18)
 # Block tolerance, as for int8 weights. Quantisation is a step function: where the kernels'
 # bfloat16 intermediates (q, k, v, the residual stream) differ from the oracle's float64 values
 # by delta, a code moves by one step s with probability about delta / s, so the difference
@@ -154,9 +155,9 @@ def stored_w8a8_mlp(x1, w, mod):
     return b16(x1 + mod[5] * (h @ w["down"].T))
 
 
+@pytest.mark.parametrize("wl", [SMALL_A8, MID_A8], ids=lambda w: w.name)
 @pytest.mark.parametrize("merged", [False, True])
-def test_block_w8a8_all_rows(B, merged, record):
-    wl = SMALL_A8
+def test_block_w8a8_all_rows(B, wl, merged, record):
     og = oracle_geom(wl, merged)
     cfg, g = binding_cfg(wl), binding_geom(wl, merged)
     x = synth.storage_values(synth.normal(wl.seed_base, 77, (og.n_tokens, wl.d_model)), "bf16")
