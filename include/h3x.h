@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   H3X_OK = 0,
   H3X_EINVAL = 1,     /* an argument is out of range or inconsistent */
-  H3X_ENOTSUP = 2,    /* valid, but a shape/dtype combination this build has no kernel for */
+  H3X_ENOTSUP = 2,    /* valid, but a shape/dtype combination the library has no kernel for */
   H3X_EWORKSPACE = 3, /* workspace smaller than the matching *_workspace_bytes() */
   H3X_EHIP = 4        /* a HIP launch or runtime call failed */
 } h3x_status;
