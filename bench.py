@@ -155,15 +155,21 @@ def bench_block(args, B, torch, synth, weight="bf16"):
     torch.cuda.synchronize()
     # Timed region: K steps; every launch inside is bracketed by HIP events on its own stream
     # (the per-kernel durations below), the wall clock gives the step time.
+    # Events between consecutive steps on the launch stream give each step's own duration.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     B.profile_begin()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         B.dit_block_forward(cfg, g, pb, modd, x, ws)
+        evs[i + 1].record()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     prof = B.profile_end()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     flops = block_flops(n, d, f)
-    log(f"[bench] block {ms:.3f} ms  {flops / ms / 1e9:.1f} TFLOP/s")
+    log(f"[bench] block {ms:.3f} ms  {flops / ms / 1e9:.1f} TFLOP/s "
+        f"(per step: min {per_step[0]:.3f}, median {per_step[len(per_step) // 2]:.3f} ms)")
     if args.copy_calib:
         # A plain copy of known size, for calibrating hardware byte counters.
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -202,7 +208,8 @@ def bench_block(args, B, torch, synth, weight="bf16"):
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": gemm_peak,
             "unit": "TFLOP/s" if weight != "i8a8" else "TOP/s", "frac": round(achieved / gemm_peak, 4),
             "traffic": traffic, "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": dom_ms}
-    state = {"raw": raw, "mod": mod, "x": x_host, "w": w}
+    state = {"raw": raw, "mod": mod, "x": x_host, "w": w,
+             "step_ms": {"min": round(per_step[0], 4), "median": round(per_step[len(per_step) // 2], 4)}}
     return ms, flops, kern, roof, state
 
 
@@ -490,6 +497,7 @@ def main():
                    "d_model": w.d_model, "heads": w.n_heads, "head_dim": w.head_dim,
                    "ffn_inner": w.ffn_inner, "tokens": w.n_tokens, "block_flops": flops},
         "frac_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "block_step_ms": state["step_ms"],
         "roofline": roof,
         "hbm_copy_gbs": round(copy_gbs, 1),
         "mfma_probe": probe,
