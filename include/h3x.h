@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define H3X_ABI_VERSION 3
+#define H3X_ABI_VERSION 4
 
 typedef enum {
   H3X_OK = 0,
@@ -92,10 +92,9 @@ typedef struct {
   int32_t merged;
 } h3x_geom;
 
-/* Packed weights of one block (device pointers, produced by h3x_pack_weights or
- * h3x_pack_int8_weights). For H3X_I8 and H3X_I8A8 the s_* pointers hold one bfloat16 scale per
- * packed row;
- * for F32 / BF16 weights they must be NULL. */
+/* Packed weights of one block (device pointers, produced by h3x_pack_weights_bf16 /
+ * h3x_pack_weights_f32 or h3x_pack_int8_weights). For H3X_I8 and H3X_I8A8 the s_* pointers hold
+ * one bfloat16 scale per packed row; for F32 / BF16 weights they must be NULL. */
 typedef struct {
   const void *qkv, *out, *gate_up, *down;
   const void *s_qkv, *s_out, *s_gate_up, *s_down;
@@ -126,10 +125,14 @@ typedef struct {
                                        only on steps fresh for period k (h3x_step_is_fresh); on
                                        the others they are replaced by x + core_delta. Needs
                                        reuse == 1 (the two are exclusive: siami.tw control
-                                       table) and token reduction off. */
+                                       table, row "核心復用"). With token reduction the core
+                                       must lie wholly inside tr_first..tr_last or wholly
+                                       outside it (else H3X_EINVAL). */
   int32_t core_first, core_last;    /* 0 <= core_first <= core_last < n_blocks */
   float *core_delta;                /* dev [(Nv + Na + Nt) x d] float32: written on core-fresh
-                                       steps (x after the core - x before), read on the others */
+                                       steps (x after the core - x before), read on the others;
+                                       a core inside the reduced blocks uses only the first
+                                       (Nv / 2 + Na + Nt) x d values (merged rows) */
 } h3x_step;
 
 int32_t h3x_abi_version(void);
@@ -153,27 +156,39 @@ int64_t h3x_geom_tokens(const h3x_geom *geom);
  * I8A8 codes use the BF16 byte layout with 64 codes per slab row: slab (r / 256, c / 64) at
  * ((r / 256) * (cols / 64) + c / 64) * 16384, row rr holding 64 bytes in four 16-byte chunks
  * placed at q ^ ((rr >> 2) & 3) (one 64-wide K step of the int8 GEMM).
+ * `rows` x `cols` is the shape of the master (source) weight and must be the shape `kind` has
+ * for cfg: H3X_W_QKV 3d x d, H3X_W_OUT d x d, H3X_W_GATE_UP 2F x d, H3X_W_DOWN d x F (the
+ * redundant pair is a check on the caller's tensor: a mismatch is H3X_EINVAL, and 0 bytes here).
  * Packed size in bytes for the cfg's weight type (I8, I8A8: the codes; scales are
  * h3x_packed_scale_count() bfloat16 values in packed row order). */
-size_t h3x_packed_weight_bytes(const h3x_block_cfg *cfg, int32_t kind);
+size_t h3x_packed_weight_bytes(const h3x_block_cfg *cfg, int32_t kind, int64_t rows, int64_t cols);
 int64_t h3x_packed_rows(const h3x_block_cfg *cfg, int32_t kind);
 int64_t h3x_packed_scale_count(const h3x_block_cfg *cfg, int32_t kind);
 
-/* Pack one F32 or BF16 master weight (dev, cfg->weight type; for I8 configs use the next call)
- * of the shape given by `kind` into `packed` (dev, h3x_packed_weight_bytes). */
-h3x_status h3x_pack_weights(const h3x_block_cfg *cfg, int32_t kind, const void *w,
-                            void *packed, void *stream);
+/* Pack one bfloat16 master weight w (dev [rows x cols] bfloat16, cfg->weight H3X_BF16) into
+ * `packed` (dev, h3x_packed_weight_bytes bytes, not overlapping w) in the slab order above: a
+ * pure permutation, bit-exact. The weights are laid out once, ahead of every run, in the order
+ * the matrix cores read them, so that the block never re-arranges them (the pages' engine keeps
+ * its weights where they are loaded instead of copying them: jdon.com,
+ * "330亿参数是什么概念"). h3x_pack_weights_f32 is the same for the float32 configuration
+ * (cfg->weight H3X_F32, row-major packed rows). */
+h3x_status h3x_pack_weights_bf16(const h3x_block_cfg *cfg, int32_t kind, const void *w,
+                                 int64_t rows, int64_t cols, void *packed, void *stream);
+h3x_status h3x_pack_weights_f32(const h3x_block_cfg *cfg, int32_t kind, const void *w,
+                                int64_t rows, int64_t cols, void *packed, void *stream);
 
-/* Per-output-channel symmetric int8 quantisation of a bfloat16 master weight (dev) into int8
- * codes `q_packed` (dev, packed row order) and bfloat16 scales `scale_bf16` (dev, one per packed
- * row). Per source row r: a = max|W[r,:]|; a == 0 gives scale 0 and zero codes; otherwise
- * s = bf16(a / 127) (IEEE float32 division, round to nearest even, then round to bfloat16);
- * s == 0 (underflow) gives zero codes; else q = clamp(rint(W / s), -127, 127) with an IEEE
- * float32 division by the stored s. Pages: 21cto.com "M5 Max 生产环境实测数据" item 4; siami.tw
- * "2. 數據會說話". cfg->weight must be H3X_I8 or H3X_I8A8 (cfg->act H3X_BF16); the two differ
- * only in the order in which the codes are stored. */
+/* Per-output-channel symmetric int8 quantisation of a bfloat16 master weight (dev [rows x cols])
+ * into int8 codes `q_packed` (dev, packed row order, h3x_packed_weight_bytes bytes) and
+ * bfloat16 scales `scale_bf16` (dev, one per packed row). Per source row r: a = max|W[r,:]|;
+ * a == 0 gives scale 0 and zero codes; otherwise s = bf16(a / 127) (IEEE float32 division,
+ * round to nearest even, then round to bfloat16); s == 0 (underflow) gives zero codes; else
+ * q = clamp(rint(W / s), -127, 127) with an IEEE float32 division by the stored s. Bit-exact
+ * (no choice is left to the kernel). Pages: 21cto.com "M5 Max 生产环境实测数据" item 4;
+ * siami.tw "2. 數據會說話". cfg->weight must be H3X_I8 or H3X_I8A8 (cfg->act H3X_BF16); the two
+ * differ only in the order in which the codes are stored. */
 h3x_status h3x_pack_int8_weights(const h3x_block_cfg *cfg, int32_t kind, const void *w_bf16,
-                                 void *q_packed, void *scale_bf16, void *stream);
+                                 int64_t rows, int64_t cols, void *q_packed, void *scale_bf16,
+                                 void *stream);
 
 /* ------------------------------------------------------------------ one block
  * x (dev [N x d], act type, in place): x1 = x + gate1 * (attn(rope(qkv(y))) @ W_out^T) with

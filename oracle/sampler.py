@@ -38,7 +38,9 @@ Variants the pages name (readings where they give no formula):
   every step runs the outer blocks; the core blocks ``core_first..core_last`` run only on steps
   that are fresh for the core period k (the same rule as whole reuse), where the change they
   make to the activations, ``delta = x_after - x_before``, is kept; on the other steps the core
-  is replaced by ``x + delta``.
+  is replaced by ``x + delta``. Core reuse combines with token reduction (the pages make it
+  exclusive only with whole-velocity reuse): the core then lies wholly inside the reduced
+  blocks, and its change is kept in the merged geometry, or wholly outside them.
 """
 from __future__ import annotations
 
@@ -133,11 +135,18 @@ def dit_eval(x0, blocks, mods, geom: Geometry, n_heads: int, act: str,
 
     core: None, or (first, last, fresh, delta): with fresh the core blocks run and
     ``x_after - x_before`` is returned as the new delta; otherwise they are replaced by
-    ``x + delta``. Returns x, or (x, delta) when core is given.
+    ``x + delta``. With token reduction the core lies wholly inside the reduced range (its
+    delta then has the merged row count) or wholly outside it. Returns x, or (x, delta) when
+    core is given.
     """
     x = np.asarray(x0, np.float64)
     g = geom
     n_blocks = len(blocks)
+    if core is not None and tr_first >= 0:
+        first, last = core[0], core[1]
+        inside = tr_first <= first and last <= tr_last
+        if not (inside or last < tr_first or first > tr_last):
+            raise ValueError("the core blocks straddle a token-reduction boundary")
     delta_out = None
     b = 0
     while b < n_blocks:

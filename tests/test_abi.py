@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(B):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(B.SIGNATURES), set(names) ^ set(B.SIGNATURES)
-    assert L.h3x_abi_version() == 3
+    assert L.h3x_abi_version() == 4
 
 
 def test_step_struct_layout_matches_c(B, tmp_path):
@@ -159,7 +159,15 @@ def test_denoise_step_rejects_before_launch(B):
     assert call(step=1, reuse=2, ex=0.5) == 1 and "v_prev" in _last(B)
     assert call(ex=math.nan) == 1 and call(vp=FAKE + 8) == 1
     assert call(core=2, c0=1, c1=2, reuse=2) == 1 and "exclusive" in _last(B)
-    assert call(core=2, c0=1, c1=2, trf=1, trl=2) == 1
+    # Core reuse with token reduction: the core wholly inside or wholly outside the reduced
+    # blocks passes validation (and fails on the too-small workspace after it); straddling fails.
+    for c0, c1, trf, trl, ok in ((1, 2, 1, 2, True), (2, 2, 1, 3, True), (0, 0, 1, 3, True),
+                                 (3, 3, 1, 2, True), (0, 1, 1, 2, False), (1, 3, 1, 2, False),
+                                 (0, 3, 1, 2, False)):
+        st = call(core=2, c0=c0, c1=c1, trf=trf, trl=trl, ws=need - 1)
+        assert st == (3 if ok else 1), (c0, c1, trf, trl, _last(B))
+        if not ok:
+            assert "straddle" in _last(B)
     assert call(core=2, c0=2, c1=1) == 1 and call(core=2, c0=1, c1=4) == 1 and call(core=-1) == 1
     assert call(core=2, c0=1, c1=2, cd=None) == 1 and call(core=2, c0=1, c1=2, cd=FAKE + 4) == 1
 
@@ -201,22 +209,71 @@ def test_workspace_and_packing_sizes(B):
     assert base <= ws < base + (1 << 20)
     gm = B.Geom(6, 32, 32, 256, 512, 1)
     assert L.h3x_block_workspace_bytes(ctypes.byref(c), ctypes.byref(gm)) < ws
-    assert L.h3x_packed_weight_bytes(ctypes.byref(c), 0) == 3 * 6144 * 6144 * 2
-    assert L.h3x_packed_weight_bytes(ctypes.byref(c), 2) == 2 * 24576 * 6144 * 2
+    assert L.h3x_packed_weight_bytes(ctypes.byref(c), 0, 3 * 6144, 6144) == 3 * 6144 * 6144 * 2
+    assert L.h3x_packed_weight_bytes(ctypes.byref(c), 2, 2 * 24576, 6144) == 2 * 24576 * 6144 * 2
+    assert L.h3x_packed_weight_bytes(ctypes.byref(c), 2, 24576, 6144) == 0  # not the kind's shape
+    assert L.h3x_packed_weight_bytes(ctypes.byref(c), 3, 24576, 6144) == 0  # transposed
     c8 = _cfg(B, d_model=6144, n_heads=48, ffn_inner=24576, weight="i8")
-    assert L.h3x_packed_weight_bytes(ctypes.byref(c8), 3) == 6144 * 24576
+    assert L.h3x_packed_weight_bytes(ctypes.byref(c8), 3, 6144, 24576) == 6144 * 24576
     assert L.h3x_packed_scale_count(ctypes.byref(c8), 2) == 2 * 24576
-    assert L.h3x_packed_weight_bytes(ctypes.byref(c8), 9) == 0
+    assert L.h3x_packed_weight_bytes(ctypes.byref(c8), 9, 6144, 6144) == 0
     # W8A8: the same codes and scales, plus one int8 code per projection-input element and a
     # float32 scale per row ([Npad x max(d, F)] bytes + 4 Npad).
     ca = _cfg(B, d_model=6144, n_heads=48, ffn_inner=24576, weight="i8a8")
-    assert L.h3x_packed_weight_bytes(ctypes.byref(ca), 3) == 6144 * 24576
+    assert L.h3x_packed_weight_bytes(ctypes.byref(ca), 3, 6144, 24576) == 6144 * 24576
     assert L.h3x_packed_scale_count(ctypes.byref(ca), 2) == 2 * 24576
     wa = L.h3x_block_workspace_bytes(ctypes.byref(ca), ctypes.byref(g))
     assert wa - ws == 6912 * 24576 + 6912 * 4
     # int8 weights (W8A16): room to widen the largest matrix (gate/up, 2F x d) to bfloat16.
     w8 = L.h3x_block_workspace_bytes(ctypes.byref(c8), ctypes.byref(g))
     assert w8 - ws == 2 * 24576 * 6144 * 2
+
+
+def test_pack_calls_reject_before_launch(B):
+    """The packing calls check the weight type, the caller's source shape and the pointers."""
+    L = B.lib()
+    c, cf, c8 = _cfg(B), _cfg(B, act="f32", weight="f32", head_dim=64, n_heads=8), _cfg(B, weight="i8")
+    d, f = 512, 768
+    ok_shapes = {0: (3 * d, d), 1: (d, d), 2: (2 * f, d), 3: (d, f)}
+    for kind, (r, cc) in ok_shapes.items():
+        assert L.h3x_packed_weight_bytes(ctypes.byref(c), kind, r, cc) == r * cc * 2
+        assert L.h3x_pack_weights_bf16(ctypes.byref(c), kind, FAKE, r + 1, cc, FAKE * 2, None) == 1
+        assert "needs" in _last(B)
+        if r != cc:  # the transposed shape
+            assert L.h3x_pack_weights_bf16(ctypes.byref(c), kind, FAKE, cc, r, FAKE * 2, None) == 1
+        assert L.h3x_pack_int8_weights(ctypes.byref(c8), kind, FAKE, r, cc + 64, FAKE * 2, FAKE * 3, None) == 1
+    assert L.h3x_pack_weights_bf16(ctypes.byref(cf), 1, FAKE, d, d, FAKE * 2, None) == 1  # F32 cfg
+    assert L.h3x_pack_weights_f32(ctypes.byref(c), 1, FAKE, d, d, FAKE * 2, None) == 1    # BF16 cfg
+    assert L.h3x_pack_weights_bf16(ctypes.byref(c8), 1, FAKE, d, d, FAKE * 2, None) == 1  # I8 cfg
+    assert L.h3x_pack_int8_weights(ctypes.byref(c), 1, FAKE, d, d, FAKE * 2, FAKE * 3, None) == 1
+    assert L.h3x_pack_weights_bf16(ctypes.byref(c), 1, FAKE, d, d, FAKE, None) == 1       # in place
+    assert L.h3x_pack_weights_bf16(ctypes.byref(c), 1, FAKE + 8, d, d, FAKE * 2, None) == 1
+    assert L.h3x_pack_int8_weights(ctypes.byref(c8), 1, FAKE, d, d, FAKE * 2, None, None) == 1
+    assert L.h3x_pack_weights_bf16(ctypes.byref(c), 4, FAKE, d, d, FAKE * 2, None) == 1
+
+
+# The calls the boundary's contract names (a C ABI of plain pointers and sizes), with their
+# argument counts: the library must export each of them under that name.
+CONTRACT = {
+    "h3x_block_workspace_bytes": 2, "h3x_packed_weight_bytes": 4, "h3x_pack_weights_bf16": 7,
+    "h3x_pack_int8_weights": 8, "h3x_dit_block_forward": 8, "h3x_step_is_fresh": 3,
+    "h3x_step_workspace_bytes": 2, "h3x_denoise_step": 9, "h3x_status_string": 1,
+    "h3x_last_error": 0,
+}
+
+
+def test_contract_names_and_arities(B):
+    for name, nargs in CONTRACT.items():
+        assert name in B.SIGNATURES, name
+        assert len(B.SIGNATURES[name][1]) == nargs, name
+        assert hasattr(B.lib(), name), name
+    # Argument counts as the C header declares them (parsed from the prototype).
+    src = re.sub(r"/\*.*?\*/", "", open(HEADERS[0]).read(), flags=re.S)
+    for name, nargs in CONTRACT.items():
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", src)
+        assert m, name
+        args = [a for a in m.group(1).split(",") if a.strip() and a.strip() != "void"]
+        assert len(args) == nargs, (name, args)
 
 
 def test_w8a8_kernel_level_contract(B):

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import synth
-from oracle import sampler
+from oracle import sampler, tokred
 from _util import binding_cfg, binding_geom, oracle_geom, packed_block, rel_l2, to_dev
 from test_gpu_kernels import SMALL
 
@@ -109,11 +109,15 @@ def test_fresh_step_moves_velocity_to_v_prev(B):
     assert not np.array_equal(vd.cpu().numpy(), old)
 
 
+@pytest.mark.parametrize("tr", [(-1, -1), (0, 3), (1, 2)], ids=["no_tr", "tr0_3", "tr1_2"])
 @pytest.mark.parametrize("wl", [synth.TINY, SMALL], ids=lambda w: w.name)
-def test_core_reuse_chain(B, wl, record):
+def test_core_reuse_chain(B, wl, tr, record):
     """Four blocks, core = blocks 1..2 refreshed every 2nd step: steps 0 (core fresh), 1 (core
-    reused), 2 (the last step: fresh), each checked against the oracle from the oracle's state."""
+    reused), 2 (the last step: fresh), each checked against the oracle from the oracle's state.
+    With token reduction over blocks 0..3 or 1..2 the core runs on the merged sequence and its
+    kept change has the merged row count."""
     wl, cfg, g, og, b64, arr, c, ws = _setup(B, wl, 4)
+    n_keep = og.as_merged().n_tokens if tr[0] >= 0 else og.n_tokens
     n_steps, k = 3, 2
     sig = sampler.sigma_grid(n_steps)
     z = synth.initial_state(wl)
@@ -126,13 +130,14 @@ def test_core_reuse_chain(B, wl, record):
         mods = _mods(wl, i, 4)
         B.denoise_step(cfg, g, i, n_steps, 1, float(sig[i]), float(sig[i + 1]), arr,
                        torch.from_numpy(np.stack(mods)).cuda(), zd, cdev, vd, ws,
-                       core_reuse=k, core_first=1, core_last=2, core_delta=dd)
+                       tr_first=tr[0], tr_last=tr[1], core_reuse=k, core_first=1, core_last=2, core_delta=dd)
         torch.cuda.synchronize()
         z_next, v, _, delta = sampler.denoise_step_full(z, c, v, b64, mods, og, wl.n_heads, wl.act, i, n_steps, 1,
-                                                        sig[i], sig[i + 1], core=(k, 1, 2, delta))
+                                                        sig[i], sig[i + 1], tr_first=tr[0], tr_last=tr[1],
+                                                        core=(k, 1, 2, delta))
         zg = zd.cpu().numpy().astype(np.float64)
         e = rel_l2(zg - z, z_next.astype(np.float64) - z)
-        record(f"core_reuse[{wl.name}] step {i} change", e, 3 * TOL[wl.act])
+        record(f"core_reuse[{wl.name},tr={tr}] step {i} change", e, 3 * TOL[wl.act])
         assert e < 3 * TOL[wl.act], (i, e)
         if i == 0:
             # The kept change is a difference of two stored residual streams: besides 3x the
@@ -140,9 +145,12 @@ def test_core_reuse_chain(B, wl, record):
             # each for bfloat16), measured against the change itself.
             unit = 2.0 ** -9 if wl.act == "bf16" else 2.0 ** -24
             x0 = np.concatenate([z, c]).astype(np.float64)
+            if tr[0] >= 0:
+                x0 = tokred.merge(x0, og, wl.act)
+            assert delta.shape == (n_keep, wl.d_model)
             bound = 3 * TOL[wl.act] + 2 * unit / np.sqrt(3) * np.linalg.norm(x0) / np.linalg.norm(delta) * 1.5
-            ed = rel_l2(dd.cpu().numpy(), delta)
-            record(f"core_reuse[{wl.name}] delta", ed, bound)
+            ed = rel_l2(dd.cpu().numpy()[:n_keep], delta)
+            record(f"core_reuse[{wl.name},tr={tr}] delta", ed, bound)
             assert ed < bound
         z = z_next
         zd.copy_(torch.from_numpy(z))

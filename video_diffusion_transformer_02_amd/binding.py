@@ -93,11 +93,12 @@ SIGNATURES = {
     "h3x_status_string": (ctypes.c_char_p, [_I32]),
     "h3x_last_error": (ctypes.c_char_p, []),
     "h3x_geom_tokens": (_I64, [_GEOM]),
-    "h3x_packed_weight_bytes": (_SZ, [_CFG, _I32]),
+    "h3x_packed_weight_bytes": (_SZ, [_CFG, _I32, _I64, _I64]),
     "h3x_packed_rows": (_I64, [_CFG, _I32]),
     "h3x_packed_scale_count": (_I64, [_CFG, _I32]),
-    "h3x_pack_weights": (_I32, [_CFG, _I32, _P, _P, _P]),
-    "h3x_pack_int8_weights": (_I32, [_CFG, _I32, _P, _P, _P, _P]),
+    "h3x_pack_weights_bf16": (_I32, [_CFG, _I32, _P, _I64, _I64, _P, _P]),
+    "h3x_pack_weights_f32": (_I32, [_CFG, _I32, _P, _I64, _I64, _P, _P]),
+    "h3x_pack_int8_weights": (_I32, [_CFG, _I32, _P, _I64, _I64, _P, _P, _P]),
     "h3x_block_workspace_bytes": (_SZ, [_CFG, _GEOM]),
     "h3x_dit_block_forward": (_I32, [_CFG, _GEOM, ctypes.POINTER(BlockWeights), _P, _P, _P, _SZ, _P]),
     "h3x_step_is_fresh": (_I32, [_I32, _I32, _I32]),
@@ -194,21 +195,34 @@ def packed_rows(cfg: BlockCfg, kind: int) -> int:
     return lib().h3x_packed_rows(ctypes.byref(cfg), kind)
 
 
+def _shape2(w: torch.Tensor):
+    if w.dim() != 2:
+        raise H3xError("expected a 2-D master weight")
+    return w.shape[0], w.shape[1]
+
+
+def packed_weight_bytes(cfg: BlockCfg, kind: int, rows: int, cols: int) -> int:
+    return lib().h3x_packed_weight_bytes(ctypes.byref(cfg), kind, rows, cols)
+
+
 def pack_weights(cfg: BlockCfg, kind: int, w: torch.Tensor) -> torch.Tensor:
-    nbytes = lib().h3x_packed_weight_bytes(ctypes.byref(cfg), kind)
-    packed = torch.empty(nbytes // w.element_size(), dtype=w.dtype, device=w.device)
-    _check(lib().h3x_pack_weights(ctypes.byref(cfg), kind, _p(w), _p(packed), _stream()), "pack_weights")
+    """bfloat16 (h3x_pack_weights_bf16) or float32 (h3x_pack_weights_f32) packing by cfg.weight."""
+    rows, cols = _shape2(w)
+    nbytes = packed_weight_bytes(cfg, kind, rows, cols)
+    packed = torch.empty(max(nbytes // w.element_size(), 1), dtype=w.dtype, device=w.device)
+    fn = lib().h3x_pack_weights_bf16 if cfg.weight == BF16 else lib().h3x_pack_weights_f32
+    _check(fn(ctypes.byref(cfg), kind, _p(w), rows, cols, _p(packed), _stream()), "pack_weights")
     return packed.view(packed_rows(cfg, kind), -1)
 
 
 def pack_int8_weights(cfg: BlockCfg, kind: int, w_bf16: torch.Tensor):
-    rows = packed_rows(cfg, kind)
-    q = torch.empty(lib().h3x_packed_weight_bytes(ctypes.byref(cfg), kind), dtype=torch.int8,
-                    device=w_bf16.device)
-    s = torch.empty(rows, dtype=torch.bfloat16, device=w_bf16.device)
-    _check(lib().h3x_pack_int8_weights(ctypes.byref(cfg), kind, _p(w_bf16), _p(q), _p(s), _stream()),
+    rows, cols = _shape2(w_bf16)
+    prow = packed_rows(cfg, kind)
+    q = torch.empty(max(packed_weight_bytes(cfg, kind, rows, cols), 1), dtype=torch.int8, device=w_bf16.device)
+    s = torch.empty(max(prow, 1), dtype=torch.bfloat16, device=w_bf16.device)
+    _check(lib().h3x_pack_int8_weights(ctypes.byref(cfg), kind, _p(w_bf16), rows, cols, _p(q), _p(s), _stream()),
            "pack_int8_weights")
-    return q.view(rows, -1), s
+    return q.view(prow, -1), s
 
 
 def pack_block(cfg: BlockCfg, w: dict) -> PackedBlock:

@@ -436,11 +436,11 @@ int64_t h3x_packed_rows(const h3x_block_cfg* c, int32_t kind) {
   return r;
 }
 
-size_t h3x_packed_weight_bytes(const h3x_block_cfg* c, int32_t kind) {
+size_t h3x_packed_weight_bytes(const h3x_block_cfg* c, int32_t kind, int64_t rows, int64_t cols) {
   if (check_cfg(c) != H3X_OK) return 0;
   int64_t r, cc;
   weight_shape(c, kind, &r, &cc);
-  if (r < 0) return 0;
+  if (r < 0 || rows != r || cols != cc) return 0;
   const size_t es = int8_weights(c) ? 1 : (c->weight == H3X_BF16 ? 2 : 4);
   return static_cast<size_t>(r) * cc * es;
 }
@@ -453,31 +453,55 @@ int64_t h3x_packed_scale_count(const h3x_block_cfg* c, int32_t kind) {
   return int8_weights(c) ? r : 0;
 }
 
-h3x_status h3x_pack_weights(const h3x_block_cfg* c, int32_t kind, const void* w, void* packed,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+// Shared checks of the packing calls: kind, the caller's source shape, pointers.
+h3x_status check_pack(const h3x_block_cfg* c, int32_t kind, int64_t rows, int64_t cols, const void* w,
+                      const void* out, const char* who) {
+  int64_t r, cc;
+  weight_shape(c, kind, &r, &cc);
+  if (r < 0) return fail(H3X_EINVAL, std::string(who) + ": bad kind");
+  if (rows != r || cols != cc)
+    return fail(H3X_EINVAL, std::string(who) + ": source is " + std::to_string(rows) + " x " + std::to_string(cols) +
+                                ", the kind needs " + std::to_string(r) + " x " + std::to_string(cc));
+  if (!w || !out || !aligned16(w) || !aligned16(out)) return fail(H3X_EINVAL, std::string(who) + ": NULL or misaligned pointer");
+  if (w == out) return fail(H3X_EINVAL, std::string(who) + ": in-place packing is not supported");
+  return H3X_OK;
+}
+
+h3x_status pack_plain(const h3x_block_cfg* c, int32_t kind, const void* w, int64_t rows, int64_t cols,
+                      void* packed, void* stream, int want, const char* who) {
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
-  if (int8_weights(c)) return fail(H3X_EINVAL, "pack_weights: use h3x_pack_int8_weights for I8 / I8A8 configs");
-  int64_t rows, cols;
-  weight_shape(c, kind, &rows, &cols);
-  if (rows < 0) return fail(H3X_EINVAL, "pack_weights: bad kind");
-  if (!w || !packed || !aligned16(w) || !aligned16(packed)) return fail(H3X_EINVAL, "pack_weights: NULL or misaligned pointer");
-  if (w == packed) return fail(H3X_EINVAL, "pack_weights: in-place packing is not supported");
+  if (c->weight != want)
+    return fail(H3X_EINVAL, std::string(who) + (want == H3X_BF16 ? ": cfg->weight must be BF16" : ": cfg->weight must be F32"));
+  if ((st = check_pack(c, kind, rows, cols, w, packed, who)) != H3X_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   H3X_LAUNCH("pack", s, launch_pack(c->weight, kind, rows, cols, w, packed, s));
   return H3X_OK;
 }
+}  // namespace
 
-h3x_status h3x_pack_int8_weights(const h3x_block_cfg* c, int32_t kind, const void* w_bf16,
-                                 void* q_packed, void* scale_bf16, void* stream) {
+extern "C" {
+
+h3x_status h3x_pack_weights_bf16(const h3x_block_cfg* c, int32_t kind, const void* w, int64_t rows,
+                                 int64_t cols, void* packed, void* stream) {
+  return pack_plain(c, kind, w, rows, cols, packed, stream, H3X_BF16, "pack_weights_bf16");
+}
+
+h3x_status h3x_pack_weights_f32(const h3x_block_cfg* c, int32_t kind, const void* w, int64_t rows,
+                                int64_t cols, void* packed, void* stream) {
+  return pack_plain(c, kind, w, rows, cols, packed, stream, H3X_F32, "pack_weights_f32");
+}
+
+h3x_status h3x_pack_int8_weights(const h3x_block_cfg* c, int32_t kind, const void* w_bf16, int64_t rows,
+                                 int64_t cols, void* q_packed, void* scale_bf16, void* stream) {
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
   if (!int8_weights(c)) return fail(H3X_EINVAL, "pack_int8_weights: cfg->weight must be I8 or I8A8");
-  int64_t rows, cols;
-  weight_shape(c, kind, &rows, &cols);
-  if (rows < 0) return fail(H3X_EINVAL, "pack_int8_weights: bad kind");
-  if (!w_bf16 || !q_packed || !scale_bf16 || !aligned16(w_bf16) || !aligned16(q_packed))
-    return fail(H3X_EINVAL, "pack_int8_weights: NULL or misaligned pointer");
+  if ((st = check_pack(c, kind, rows, cols, w_bf16, q_packed, "pack_int8_weights")) != H3X_OK) return st;
+  if (!scale_bf16) return fail(H3X_EINVAL, "pack_int8_weights: NULL scale pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
   H3X_LAUNCH("pack_int8", s, launch_pack_int8(kind, rows, cols, w_bf16, static_cast<int8_t*>(q_packed),
                                               static_cast<uint16_t*>(scale_bf16), c->weight == H3X_I8A8, s));
@@ -565,9 +589,16 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
   if (st_->core_reuse < 0) return fail(H3X_EINVAL, "denoise_step: negative core_reuse");
   if (core_on) {
     if (st_->reuse != 1) return fail(H3X_EINVAL, "denoise_step: core reuse and whole-velocity reuse are exclusive");
-    if (st_->tr_first != -1 || st_->tr_last != -1) return fail(H3X_EINVAL, "denoise_step: core reuse needs token reduction off");
     if (st_->core_first < 0 || st_->core_first > st_->core_last || st_->core_last >= st_->n_blocks)
       return fail(H3X_EINVAL, "denoise_step: need 0 <= core_first <= core_last < n_blocks");
+    // With token reduction the core runs wholly in one geometry: inside the reduced blocks (its
+    // kept change then has the merged row count) or wholly before or after them.
+    if (st_->tr_first >= 0) {
+      const bool inside = st_->tr_first <= st_->core_first && st_->core_last <= st_->tr_last;
+      const bool outside = st_->core_last < st_->tr_first || st_->core_first > st_->tr_last;
+      if (!inside && !outside)
+        return fail(H3X_EINVAL, "denoise_step: the core blocks straddle a token-reduction boundary");
+    }
     if (!st_->core_delta || !aligned16(st_->core_delta)) return fail(H3X_EINVAL, "denoise_step: NULL or misaligned core_delta");
   }
   if (fresh) {
@@ -613,18 +644,8 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
   H3X_LAUNCH("assemble", s, launch_assemble(c->act, n_state, g->n_text, c->d_model, z, text, lay.x, s));
   const size_t mod_stride = 6 * static_cast<size_t>(c->d_model);
   const bool core_fresh = core_on && h3x_step_is_fresh(st_->step, st_->n_steps, st_->core_reuse) == 1;
-  const int64_t n_all = (n_state + g->n_text) * c->d_model;
   bool merged = false;
   for (int b = 0; b < st_->n_blocks; ++b) {
-    if (core_on && b == st_->core_first) {
-      if (core_fresh) {
-        H3X_LAUNCH("core_save", s, launch_core(c->act, 0, n_all, lay.x, st_->core_delta, s));
-      } else {  // the kept change of the core replaces its blocks
-        H3X_LAUNCH("core_apply", s, launch_core(c->act, 2, n_all, lay.x, st_->core_delta, s));
-        b = st_->core_last;
-        continue;
-      }
-    }
     if (use_tr && b == st_->tr_first) {
       H3X_LAUNCH("token_merge", s, launch_token_merge(c->act, geom_dev(*g), c->d_model, lay.x, lay.xm, s));
       merged = true;
@@ -633,8 +654,20 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
       H3X_LAUNCH("token_unmerge", s, launch_token_unmerge(c->act, geom_dev(*g), c->d_model, lay.xm, lay.x, s));
       merged = false;
     }
-    BlockWs bw = lay.blk;
     const h3x_geom* gb = merged ? &gm : g;
+    void* xb = merged ? lay.xm : lay.x;
+    // The core's change lives in the geometry its blocks run in (validated above: one geometry).
+    const int64_t n_cur = geom_tokens(gb) * c->d_model;
+    if (core_on && b == st_->core_first) {
+      if (core_fresh) {
+        H3X_LAUNCH("core_save", s, launch_core(c->act, 0, n_cur, xb, st_->core_delta, s));
+      } else {  // the kept change of the core replaces its blocks
+        H3X_LAUNCH("core_apply", s, launch_core(c->act, 2, n_cur, xb, st_->core_delta, s));
+        b = st_->core_last;
+        continue;
+      }
+    }
+    BlockWs bw = lay.blk;
     bw.n = geom_tokens(gb);
     bw.n_pad = round_up(bw.n, 256);
     // Re-derive the y and R1 arenas for the (smaller) merged sequence inside the unmerged ones.
@@ -650,11 +683,10 @@ h3x_status h3x_denoise_step(const h3x_block_cfg* c, const h3x_geom* g, const h3x
       m.w16 = lay.blk.w16;
       bw = m;
     }
-    if ((st = block_forward_impl(c, gb, &st_->blocks[b], st_->mod + b * mod_stride,
-                                 merged ? lay.xm : lay.x, bw, s)) != H3X_OK)
+    if ((st = block_forward_impl(c, gb, &st_->blocks[b], st_->mod + b * mod_stride, xb, bw, s)) != H3X_OK)
       return st;
     if (core_fresh && b == st_->core_last)
-      H3X_LAUNCH("core_diff", s, launch_core(c->act, 1, n_all, lay.x, st_->core_delta, s));
+      H3X_LAUNCH("core_diff", s, launch_core(c->act, 1, n_cur, xb, st_->core_delta, s));
   }
   if (merged)
     H3X_LAUNCH("token_unmerge", s, launch_token_unmerge(c->act, geom_dev(*g), c->d_model, lay.xm, lay.x, s));

@@ -17,6 +17,7 @@
 //    pieces' partial results (unnormalised O, lazy max, sum) are merged by attn_combine_kernel.
 //  * attn_f32_kernel: float32, one thread per (query, head), online softmax over keys; the
 //    k and v reads of a wave are broadcasts (all its lanes read the same key).
+#include <mutex>
 #include <math.h>
 
 #include "launch.h"
@@ -375,16 +376,19 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 int attention_slots(int requested) {
   const int cap = kAttnMaxPieceQueries / kAttnQueries;
   if (requested > 0) return requested < cap ? requested : cap;
-  static int cached[64] = {0};
+  // The compute-unit count of each device, queried once per device (thread-safe).
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static int cus[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = cus;
-  }
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return cap < 512 ? cap : 512;
+  std::call_once(once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  });
   // One eight-wave workgroup per CU (two waves per SIMD).
-  return cached[dev] < cap ? cached[dev] : cap;
+  return cus[dev] < cap ? cus[dev] : cap;
 }
 
 AttnPlan attention_plan(int64_t n_tokens, int n_heads, int slots) {
