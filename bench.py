@@ -207,7 +207,8 @@ def bench_block(args, B, torch, synth, weight="bf16"):
     traffic = measured_traffic(args.traffic) if weight == "bf16" else None
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": gemm_peak,
             "unit": "TFLOP/s" if weight != "i8a8" else "TOP/s", "frac": round(achieved / gemm_peak, 4),
-            "traffic": traffic, "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": dom_ms}
+            "traffic": traffic, "algorithmic_flops_per_launch": kflops[dom], "avg_launch_ms": dom_ms,
+            "timing": "HIP events recorded around each launch on its launch stream, inside the timed region"}
     state = {"raw": raw, "mod": mod, "x": x_host, "w": w,
              "step_ms": {"min": round(per_step[0], 4), "median": round(per_step[len(per_step) // 2], 4)}}
     return ms, flops, kern, roof, state
@@ -280,6 +281,7 @@ def cpu_baseline(args, state):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count()
+    host = host_cpu()
     reps, t0 = 0, time.perf_counter()
     while True:
         dit.block_forward(x, vals, state["mod"], geom, w.n_heads, rows=rows)
@@ -287,10 +289,40 @@ def cpu_baseline(args, state):
         if time.perf_counter() - t0 >= args.cpu_seconds:
             break
     dt = time.perf_counter() - t0
-    log(f"[bench] oracle sample: {reps} x ({r} query rows, {flops / 1e12:.3f} TFLOP) in {dt:.1f} s on {cores} threads")
+    log(f"[bench] oracle sample: {reps} x ({r} query rows, {flops / 1e12:.3f} TFLOP) in {dt:.1f} s on {cores} threads"
+        f" ({host})")
     return {"value": round(reps * flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"one block at the same shape: K/V of all {n} rows plus {r} of {n} query rows "
-                      f"({flops / 1e12:.3f} TFLOP per pass), {reps} passes in {dt:.1f} s"}
+                      f"({flops / 1e12:.3f} TFLOP per pass), {reps} passes in {dt:.1f} s",
+            "threads": "cores = BLAS threads the oracle ran on", "host": host}
+
+
+def host_cpu():
+    """The host's CPU as the oracle sees it: model name, logical CPUs, CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "logical_cpus": os.cpu_count()}
+
+
+def input_hashes(synth, state):
+    """SHA-256 (first 16 MiB, as stored) of the block benchmark's seeded inputs, so that a run can
+    be matched with the oracle's inputs."""
+    out = {"x": synth.sha256_prefix(synth.to_storage(state["x"], "bf16")),
+           "mod": synth.sha256_prefix(state["mod"])}
+    for k, v in state["raw"].items():
+        out["w_" + k] = synth.sha256_prefix(synth.to_storage(v, "bf16"))
+    return out
 
 
 def bench_denoise(args, B, torch, synth):
@@ -351,11 +383,9 @@ def bench_denoise(args, B, torch, synth):
         n_tok = wl.n_tokens
         nm = wl.n_video // 2 + wl.n_audio + wl.n_text
         bf = block_flops(n_tok, wl.d_model, wl.ffn_inner)
-        if wl.tr_first >= 0:
-            n_red = wl.tr_last - wl.tr_first + 1
-            eval_flops = (wl.n_blocks - n_red) * bf + n_red * block_flops(nm, wl.d_model, wl.ffn_inner)
-        else:
-            eval_flops = wl.n_blocks * bf
+        bf_m = block_flops(nm, wl.d_model, wl.ffn_inner)
+        per_block = [bf_m if wl.tr_first <= b <= wl.tr_last else bf for b in range(wl.n_blocks)]
+        eval_flops = sum(per_block)
         fresh_ms = float(np.mean(fresh))
         res = {"ms_per_step": round(total / wl.n_steps, 3), "total_ms": round(total, 2),
                "fresh_steps": len(fresh), "ms_per_fresh_step": round(fresh_ms, 3),
@@ -364,8 +394,8 @@ def bench_denoise(args, B, torch, synth):
         if core:
             k, first, last = core
             core_fresh = [B.step_is_fresh(i, wl.n_steps, k) for i in range(wl.n_steps)]
-            n_core = last - first + 1
-            flops = sum(eval_flops if cf else (wl.n_blocks - n_core) * bf for cf in core_fresh)
+            core_part = sum(per_block[first:last + 1])
+            flops = sum(eval_flops if cf else eval_flops - core_part for cf in core_fresh)
             res["core_fresh_steps"] = sum(core_fresh)
             res["tflops"] = round(flops / total / 1e9, 1)
         else:
@@ -393,6 +423,9 @@ def bench_denoise(args, B, torch, synth):
                                                     extrap=True)
     out["denoise_45blk_20step_core4_10_34"] = run(wl.replace(reuse=1), packed, "core reuse 4 over blocks 10..34",
                                                   core=(4, 10, 34))
+    out["denoise_45blk_20step_core4_tr10_34"] = run(synth.DENOISE45_TR.replace(reuse=1), packed,
+                                                    "core reuse 4 over blocks 10..34 with token reduction 10..34",
+                                                    core=(4, 10, 34))
     out["denoise_45blk_4step_linear_terminal_cond1"] = run(
         wl.replace(n_steps=4, reuse=1), packed, "4 steps, linear base grid of 20 + terminal step, first frame fixed",
         sched=("linear_terminal", 20.0), cond=(1, 0))
@@ -503,6 +536,7 @@ def main():
         "mfma_probe": probe,
         "sampler_kernels": sampler,
         "cpu_baseline": cpu,
+        "inputs_sha256": input_hashes(synth, state),
         "kernels": kern,
         "block_w8a8": w8a8,
         "denoise": denoise,

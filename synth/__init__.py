@@ -88,7 +88,14 @@ DENOISE45_TR = DENOISE45.replace(name="denoise_45blk_20step_reuse2_tr10_34", tr_
 INT8_50 = BLOCK.replace(name="int8w_50blk_4step_6x30x54", grid_h=30, grid_w=54, n_blocks=50,
                         weight="i8", n_steps=4, reuse=1, seed_base=4)
 
-WORKLOADS = {w.name: w for w in (TINY, TINY_SHARP, BLOCK, DENOISE45, DENOISE45_TR, INT8_50)}
+# The 45-block, 20-step, reuse-2 schedule with token reduction over blocks 10..34 at a width
+# the oracle runs end to end in seconds: d 256 (2 heads x 128), F 1024, bf16, 6 x 8 x 8 video +
+# 16 audio + 32 text tokens (432; 240 when merged).
+TINY_LONG = BLOCK.replace(name="tiny_long_bf16_45blk_20step_reuse2_tr10_34", d_model=256, n_heads=2,
+                          ffn_inner=1024, frames=6, grid_h=8, grid_w=8, n_audio=16, n_text=32,
+                          n_blocks=45, n_steps=20, reuse=2, tr_first=10, tr_last=34, seed_base=31)
+
+WORKLOADS = {w.name: w for w in (TINY, TINY_SHARP, BLOCK, DENOISE45, DENOISE45_TR, INT8_50, TINY_LONG)}
 
 
 def stream(base: int, ident: int) -> np.random.Generator:

@@ -96,3 +96,45 @@ def unslab(t, rows: int, cols: int, esize: int) -> np.ndarray:
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def stored_block(x, w, mod, geom, n_heads, rows=None, act_quant=None, act="bf16"):
+    """The oracle's block with a rounding to the storage type wherever the kernels store a
+    tensor: y, q and k (after RoPE), v, o, x1, y2, h, x2 (each value taken to float32, then
+    rounded to the storage type, as the kernels store their float32 results). Built from the
+    oracle's own functions;
+    with act_quant (W8A8) the per-row quantisation is applied to the stored projection inputs
+    y, o, y2 and h, as the kernels quantise them. rows: the output rows to form (all if None;
+    k and v always cover every row). A tighter reference than the oracle for the kernels'
+    arithmetic: what is left between the two is float32 accumulation and the bfloat16
+    probabilities inside attention, and the rounding flips these cause."""
+    from oracle import dit
+    from oracle.numeric import bf16_rne
+    if act == "bf16":  # the kernels round float32 values to bfloat16 (nearest even)
+        r = lambda a: bf16_rne(np.asarray(a, np.float64).astype(np.float32)).astype(np.float64)
+    else:
+        r = lambda a: np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
+    aq = (lambda a: a) if act_quant is None else act_quant
+    x = np.asarray(x, np.float64)
+    n, d = x.shape
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    shift1, scale1, gate1, shift2, scale2, gate2 = np.asarray(mod, np.float64)
+    wqkv = np.asarray(w["qkv"], np.float64)
+    pos, rot = geom.positions()
+    y = aq(r(dit.rms_norm_mod(x, shift1, scale1)))
+    q = r(dit.rope(y[rows] @ wqkv[:d].T, pos[rows], rot[rows], n_heads))
+    k = r(dit.rope(y @ wqkv[d:2 * d].T, pos, rot, n_heads))
+    v = r(y @ wqkv[2 * d:].T)
+    o = aq(r(dit.attention(q, k, v, n_heads)))
+    x1 = r(x[rows] + gate1 * (o @ np.asarray(w["out"], np.float64).T))
+    y2 = aq(r(dit.rms_norm_mod(x1, shift2, scale2)))
+    h = aq(r(dit.silu(y2 @ np.asarray(w["gate"], np.float64).T) * (y2 @ np.asarray(w["up"], np.float64).T)))
+    return r(x1 + gate2 * (h @ np.asarray(w["down"], np.float64).T))
+
+
+def row_rel_l2(got, ref) -> np.ndarray:
+    """Per-row relative L2 error (rows of a 2-D array)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref, axis=1)
+    return np.linalg.norm(got - ref, axis=1) / np.where(den > 0, den, 1.0)

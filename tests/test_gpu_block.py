@@ -6,7 +6,7 @@ import torch
 import synth
 from oracle import dit, sampler
 from _util import (binding_cfg, binding_geom, host, modulation, oracle_geom, packed_block, rel_l2,
-                   to_dev)
+                   row_rel_l2, stored_block, to_dev)
 from test_gpu_kernels import SMALL, SMALL_F32, SMALL_I8
 
 pytestmark = pytest.mark.gpu
@@ -35,6 +35,18 @@ def _tol(wl):
         # the storage-rounded reference below.
         return 3e-2
     return TOL["i8"] if wl.weight in ("i8", "i8a8") else TOL[wl.act]
+
+
+# Against the oracle's block with the kernels' bfloat16 stores inserted (stored_block), what is
+# left is float32-versus-float64 arithmetic and the bfloat16 probabilities inside attention: a
+# relative RMS of at most 2^-8 per probability on o (about 1.7e-3), entering through the
+# attention branch, plus the rounding flips these differences cause at the nine stores (an
+# element that lands on the other side of a rounding boundary moves by one ulp, 2^-8 relative).
+# Bound 5e-3 on the block output: three times the per-store rounding error.
+STORED_TOL = 5e-3
+# A single wrong row (a ragged tail, the last key tile) is diluted by the global norm: every
+# row on its own is held to twice the block bound.
+ROW_FACTOR = 2.0
 
 
 def branch_bound(wl, x, ref):
@@ -75,6 +87,17 @@ def test_block_all_rows(B, wl, merged, record):
     # The residual branch alone (x2 - x), which the residual does not dilute: allowed the block
     # tolerance plus the two roundings of the residual stream (x1, x2) to the storage type.
     assert rel_l2(got - x, ref - x) < branch_bound(wl, x, ref)
+    worst = row_rel_l2(got, ref)
+    record(f"block_all_rows[{wl.name},merged={merged}] worst row", worst.max(), ROW_FACTOR * _tol(wl))
+    assert worst.max() < ROW_FACTOR * _tol(wl), int(worst.argmax())
+    if wl.act == "bf16":
+        st = stored_block(x, w64, m64, og, wl.n_heads)
+        tol_st = 1e-2 if wl.name == STRONG.name else STORED_TOL
+        es, ws = rel_l2(got, st), row_rel_l2(got, st)
+        record(f"block_all_rows[{wl.name},merged={merged}] vs stored steps", es, tol_st)
+        record(f"block_all_rows[{wl.name},merged={merged}] vs stored steps worst row", ws.max(), ROW_FACTOR * tol_st)
+        assert es < tol_st
+        assert ws.max() < ROW_FACTOR * tol_st, int(ws.argmax())
 
 
 def test_block_zero_gates_is_identity_bit_exact(B):
@@ -109,6 +132,15 @@ def test_block_full_size_sampled_rows(B, record):
     record("block_full_size_sampled_rows", rel_l2(got, ref), TOL["bf16"])
     assert rel_l2(got, ref) < TOL["bf16"]
     assert rel_l2(got - x[rows], ref - x[rows]) < branch_bound(wl, x[rows], ref)
+    worst = row_rel_l2(got, ref).max()
+    record("block_full_size_sampled_rows worst row", worst, ROW_FACTOR * TOL["bf16"])
+    assert worst < ROW_FACTOR * TOL["bf16"]
+    st = stored_block(x, w64, m64, og, wl.n_heads, rows=rows)
+    es, ws = rel_l2(got, st), row_rel_l2(got, st).max()
+    record("block_full_size_sampled_rows vs stored steps", es, STORED_TOL)
+    record("block_full_size_sampled_rows vs stored steps worst row", ws, ROW_FACTOR * STORED_TOL)
+    assert es < STORED_TOL
+    assert ws < ROW_FACTOR * STORED_TOL
 
 
 # ---------------------------------------------------------------- sampler steps
@@ -179,31 +211,12 @@ def test_denoise_reused_step_reads_cache_only(B):
     np.testing.assert_array_equal(zd.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
-def storage_rounded_block(x, w, mod, geom, n_heads):
-    """The block with every stored activation (y, q, k, v, o, x1, y2, h, x2) rounded to bfloat16,
-    built from the oracle's primitives: a tighter reference for the bf16 kernels' arithmetic."""
-    from oracle.numeric import round_storage as r
-    d = x.shape[1]
-    shift1, scale1, gate1, shift2, scale2, gate2 = mod
-    pos, rot = geom.positions()
-    f64 = lambda a: np.asarray(a, np.float64)
-    y = f64(r(dit.rms_norm_mod(x, shift1, scale1), "bf16"))
-    q = f64(r(dit.rope(y @ w["qkv"][:d].T, pos, rot, n_heads), "bf16"))
-    k = f64(r(dit.rope(y @ w["qkv"][d:2 * d].T, pos, rot, n_heads), "bf16"))
-    v = f64(r(y @ w["qkv"][2 * d:].T, "bf16"))
-    o = f64(r(dit.attention(q, k, v, n_heads), "bf16"))
-    x1 = f64(r(x + gate1 * (o @ w["out"].T), "bf16"))
-    y2 = f64(r(dit.rms_norm_mod(x1, shift2, scale2), "bf16"))
-    h = f64(r(dit.silu(y2 @ w["gate"].T) * (y2 @ w["up"].T), "bf16"))
-    return f64(r(x1 + gate2 * (h @ w["down"].T), "bf16"))
-
-
 def test_block_strong_vs_storage_rounded(B, record):
     wl = STRONG
     og = oracle_geom(wl)
     x = synth.storage_values(synth.normal(wl.seed_base, 77, (og.n_tokens, wl.d_model)), "bf16")
     xd, w64, m64 = run_block(B, wl, x)
-    ref = storage_rounded_block(x, w64, m64, og, wl.n_heads)
+    ref = stored_block(x, w64, m64, og, wl.n_heads)
     e = rel_l2(host(xd), ref)
     record("block_strong_vs_storage_rounded", e, 1e-2)
     assert e < 1e-2
