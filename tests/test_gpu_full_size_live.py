@@ -166,6 +166,12 @@ def test_schedule_checkpoint_blocks(B, stack45, tr, step, record):
 # ---------------------------------------------------------------- W8A8 at 6 x 30 x 54
 A8_STORED_TOL = 2e-3  # as for the MLP half at the small shape: float32 vs float64 arithmetic only
 A8_TOL_FULL = 5e-2
+# Per row, W8A8 allows one row to re-round: a row's codes hang on its one scale, and where the
+# kernel's float32 value of the row's largest element and the reference's float64 value round to
+# different bfloat16 neighbours, the scale moves by an ulp and every code of the row re-rounds.
+# That row then differs by about a quantisation step's RMS, s / sqrt(12) with s = max|x| / 127,
+# which is 9e-3 of the row's RMS for normal rows (max about 4 RMS at 6144 columns); bound 1.5e-2.
+A8_ROW_TOL = 1.5e-2
 
 
 def stored_w8a8_mlp(x1, w, mod):
@@ -208,5 +214,5 @@ def test_w8a8_block_full_size(B, shape, record):
     st = stored_w8a8_mlp(x[rows].astype(np.float64), w64, m_mlp)
     es, worst = rel_l2(out["mlp"] - x[rows], st - x[rows]), row_rel_l2(out["mlp"], st).max()
     record(f"w8a8_block_{shape} MLP branch vs stored steps", es, A8_STORED_TOL)
-    record(f"w8a8_block_{shape} MLP vs stored steps worst row", worst, ROW_FACTOR * A8_STORED_TOL)
-    assert es < A8_STORED_TOL and worst < ROW_FACTOR * A8_STORED_TOL
+    record(f"w8a8_block_{shape} MLP vs stored steps worst row", worst, A8_ROW_TOL)
+    assert es < A8_STORED_TOL and worst < A8_ROW_TOL
