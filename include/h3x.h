@@ -207,6 +207,20 @@ h3x_status h3x_dit_block_forward(const h3x_block_cfg *cfg, const h3x_geom *geom,
                                  const h3x_block_weights *w, const float *mod, void *x,
                                  void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): h3x_dit_block_forward with the workspace taken from a
+ * device array inside the library, H3X_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the
+ * library's load until the process ends. The caller still owns x, mod and the weights. Nothing
+ * is allocated and no part of the array needs to start at zero (every region is written before
+ * it is read). A block whose h3x_block_workspace_bytes exceeds the array returns
+ * H3X_EWORKSPACE before anything is enqueued. All calls on one GPU share its array: calls that
+ * overlap in time on that GPU (different streams, or several threads) race and give undefined
+ * results; calls ordered on one stream are safe. */
+#define H3X_NOALLOC_SCRATCH_BYTES (64ull << 20)
+h3x_status h3x_dit_block_forward_noalloc(const h3x_block_cfg *cfg, const h3x_geom *geom,
+                                         const h3x_block_weights *w, const float *mod, void *x,
+                                         void *stream);
+
 /* ------------------------------------------------------------------ one sampler step
  * 1 if step i of n runs the DiT (i % reuse == 0 or i == n - 1), 0 if it reuses the cached
  * velocity, -1 on invalid arguments. Pages: siami.tw control table, row "整體 denoiser 復用". */

@@ -1,0 +1,50 @@
+"""The allocation-free block entry point (h3x_dit_block_forward_noalloc) against the block entry
+point with a caller workspace: the same kernels, so the results are identical bit for bit.
+Two calls in a row, the second with a smaller input, then an oversized block refused."""
+import ctypes
+
+import pytest
+import torch
+
+import synth
+from _util import binding_cfg, binding_geom, modulation, oracle_geom, packed_block, to_dev
+from test_gpu_kernels import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from video_diffusion_transformer_02_amd import binding
+    binding.lib()
+    return binding
+
+
+@pytest.mark.parametrize("weight", ["bf16", "i8a8"])
+def test_noalloc_matches_workspace_entry_point(B, weight):
+    big = SMALL.replace(name=f"noalloc_big_{weight}", weight=weight, seed_base=61)
+    small = big.replace(name=f"noalloc_small_{weight}", frames=1, grid_h=4, grid_w=6, n_audio=5, n_text=7,
+                        seed_base=62)
+    for wl in (big, small):
+        cfg, g, og = binding_cfg(wl), binding_geom(wl), oracle_geom(wl)
+        assert B.block_workspace_bytes(cfg, g) <= B.NOALLOC_SCRATCH_BYTES
+        _, pb = packed_block(wl, 0)
+        _, mdev = modulation(wl, 0, 0)
+        x = synth.storage_values(synth.normal(wl.seed_base, 3, (og.n_tokens, wl.d_model)), "bf16")
+        xa, xb = to_dev(x, "bf16"), to_dev(x, "bf16")
+        ws = B.alloc_workspace(B.block_workspace_bytes(cfg, g))
+        B.dit_block_forward(cfg, g, pb, mdev, xa, ws)
+        B.dit_block_forward_noalloc(cfg, g, pb, mdev, xb)
+        torch.cuda.synchronize()
+        assert torch.equal(xa.view(torch.int16), xb.view(torch.int16)), wl.name
+        assert not torch.equal(xb.view(torch.int16), to_dev(x, "bf16").view(torch.int16))
+
+
+def test_noalloc_refuses_a_block_beyond_the_scratch(B):
+    wl = synth.BLOCK
+    cfg, g = binding_cfg(wl), binding_geom(wl)
+    assert B.block_workspace_bytes(cfg, g) > B.NOALLOC_SCRATCH_BYTES
+    fake = 0x10000  # never dereferenced: the call is refused before anything is enqueued
+    w = B.BlockWeights(fake, fake, fake, fake, None, None, None, None)
+    st = B.lib().h3x_dit_block_forward_noalloc(ctypes.byref(cfg), ctypes.byref(g), ctypes.byref(w), fake, fake, None)
+    assert st == 3 and b"scratch" in B.lib().h3x_last_error()

@@ -101,6 +101,7 @@ SIGNATURES = {
     "h3x_pack_int8_weights": (_I32, [_CFG, _I32, _P, _I64, _I64, _P, _P, _P]),
     "h3x_block_workspace_bytes": (_SZ, [_CFG, _GEOM]),
     "h3x_dit_block_forward": (_I32, [_CFG, _GEOM, ctypes.POINTER(BlockWeights), _P, _P, _P, _SZ, _P]),
+    "h3x_dit_block_forward_noalloc": (_I32, [_CFG, _GEOM, ctypes.POINTER(BlockWeights), _P, _P, _P]),
     "h3x_step_is_fresh": (_I32, [_I32, _I32, _I32]),
     "h3x_sigma_schedule": (_I32, [_I32, _I32, ctypes.c_double, ctypes.POINTER(ctypes.c_float)]),
     "h3x_extrapolation_weight": (_F, [_F, _F, _F]),
@@ -254,6 +255,16 @@ def dit_block_forward(cfg: BlockCfg, geom: Geom, blk: PackedBlock, mod: torch.Te
     _check(lib().h3x_dit_block_forward(ctypes.byref(cfg), ctypes.byref(geom), ctypes.byref(ws_struct),
                                        _p(mod), _p(x), _p(ws), ws.numel(), _stream()),
            "dit_block_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # H3X_NOALLOC_SCRATCH_BYTES
+
+
+def dit_block_forward_noalloc(cfg: BlockCfg, geom: Geom, blk: PackedBlock, mod: torch.Tensor, x: torch.Tensor):
+    """The block forward on the library's own device scratch (no workspace argument)."""
+    w = blk.struct()
+    _check(lib().h3x_dit_block_forward_noalloc(ctypes.byref(cfg), ctypes.byref(geom), ctypes.byref(w), _p(mod),
+                                               _p(x), _stream()), "dit_block_forward_noalloc")
 
 
 def step_is_fresh(step: int, n_steps: int, reuse: int) -> int:

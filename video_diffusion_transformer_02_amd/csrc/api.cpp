@@ -406,6 +406,37 @@ StepWs step_layout(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* base) {
 
 }  // namespace
 
+// ---------------------------------------------------------------- allocation-free scratch
+// Device-resident workspace of h3x_dit_block_forward_noalloc: one copy per GPU, held from the
+// library's load until the process ends. Host code never passes `scratch` itself (its name is a
+// host-side stand-in, not a device address): the address is looked up per device with
+// hipGetSymbolAddress and kept.
+static __device__ __align__(256) uint8_t scratch[H3X_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+uint8_t* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+
+// The current device's copy of `scratch` (looked up once per device, with that device current).
+h3x_status scratch_ptr(uint8_t** out) {
+  int dev = 0;
+  h3x_status st = hip_check(hipGetDevice(&dev), "noalloc: hipGetDevice");
+  if (st != H3X_OK) return st;
+  if (dev < 0 || dev >= kScratchDevices) return fail(H3X_ENOTSUP, "noalloc: device index beyond 63");
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  });
+  if ((st = hip_check(g_scratch_err[dev], "noalloc: hipGetSymbolAddress(scratch)")) != H3X_OK) return st;
+  if (!g_scratch_ptr[dev]) return fail(H3X_EHIP, "noalloc: no device address for the scratch array");
+  *out = g_scratch_ptr[dev];
+  return H3X_OK;
+}
+}  // namespace
+
 // ====================================================================== exported entry points
 extern "C" {
 
@@ -525,6 +556,27 @@ h3x_status h3x_dit_block_forward(const h3x_block_cfg* c, const h3x_geom* g, cons
   const BlockWs lay = block_layout(c, g, static_cast<uint8_t*>(ws));
   if (ws_bytes < lay.bytes)
     return fail(H3X_EWORKSPACE, "block_forward: workspace needs " + std::to_string(lay.bytes) + " bytes");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = build_rope(c, g, lay.rope, s)) != H3X_OK) return st;
+  return block_forward_impl(c, g, w, mod, x, lay, s);
+}
+
+h3x_status h3x_dit_block_forward_noalloc(const h3x_block_cfg* c, const h3x_geom* g, const h3x_block_weights* w,
+                                         const float* mod, void* x, void* stream) {
+  h3x_status st = check_cfg(c);
+  if (st != H3X_OK) return st;
+  if ((st = check_geom(g)) != H3X_OK) return st;
+  if ((st = check_seq(c, geom_tokens(g))) != H3X_OK) return st;
+  if ((st = check_weights(c, w)) != H3X_OK) return st;
+  if (!mod || !x || !aligned16(mod) || !aligned16(x)) return fail(H3X_EINVAL, "block_forward_noalloc: NULL or misaligned mod / x");
+  const size_t need = block_layout(c, g, nullptr).bytes;
+  if (need > H3X_NOALLOC_SCRATCH_BYTES)
+    return fail(H3X_EWORKSPACE, "block_forward_noalloc: this block needs " + std::to_string(need) +
+                                    " bytes of workspace, beyond the " + std::to_string(H3X_NOALLOC_SCRATCH_BYTES) +
+                                    "-byte device scratch; use h3x_dit_block_forward with a workspace");
+  uint8_t* base = nullptr;
+  if ((st = scratch_ptr(&base)) != H3X_OK) return st;
+  const BlockWs lay = block_layout(c, g, base);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = build_rope(c, g, lay.rope, s)) != H3X_OK) return st;
   return block_forward_impl(c, g, w, mod, x, lay, s);
