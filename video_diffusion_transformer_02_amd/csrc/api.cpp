@@ -188,6 +188,12 @@ size_t attn_region_bytes(const h3x_block_cfg* c, int64_t n) {
   return per_tile < cap ? per_tile : cap;
 }
 
+// Address `off` bytes into a workspace. Integer arithmetic, so that a layout can also be
+// computed for base == nullptr (the size queries) without pointer arithmetic on a null pointer.
+uint8_t* at(uint8_t* base, size_t off) {
+  return reinterpret_cast<uint8_t*>(reinterpret_cast<uintptr_t>(base) + off);
+}
+
 // Activation arenas by lifetime: R2 holds y (norm before attention), then y2 (norm before the
 // MLP); R1 holds q, k, v^T and the attention output o, then the SwiGLU hidden h.
 BlockWs block_layout(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* base) {
@@ -199,23 +205,24 @@ BlockWs block_layout(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* base) {
   const size_t r1 = static_cast<size_t>(w.n_pad) * es *
                     static_cast<size_t>(c->ffn_inner > 4 * c->d_model ? c->ffn_inner : 4 * c->d_model);
   size_t off = 0;
-  w.y = base + off; off = align256(off + nd);
-  w.q = base + off; w.k = w.q + nd; w.vt = w.k + nd; w.o = w.vt + nd; w.h = w.q;
+  w.y = at(base, off); off = align256(off + nd);
+  w.q = at(base, off); w.k = at(base, off + nd); w.vt = at(base, off + 2 * nd); w.o = at(base, off + 3 * nd);
+  w.h = w.q;
   off = align256(off + r1);
-  w.rope = base + off; off = align256(off + rope_bytes(c, g));
-  w.attn = base + off; off = align256(off + attn_region_bytes(c, w.n));
+  w.rope = at(base, off); off = align256(off + rope_bytes(c, g));
+  w.attn = at(base, off); off = align256(off + attn_region_bytes(c, w.n));
   w.a8 = nullptr;
   w.a8s = nullptr;
   w.w16 = nullptr;
   if (c->weight == H3X_I8A8) {
     const size_t cols = static_cast<size_t>(c->ffn_inner > c->d_model ? c->ffn_inner : c->d_model);
-    w.a8 = base + off; off = align256(off + static_cast<size_t>(w.n_pad) * cols);
-    w.a8s = reinterpret_cast<float*>(base + off); off = align256(off + static_cast<size_t>(w.n_pad) * 4);
+    w.a8 = at(base, off); off = align256(off + static_cast<size_t>(w.n_pad) * cols);
+    w.a8s = reinterpret_cast<float*>(at(base, off)); off = align256(off + static_cast<size_t>(w.n_pad) * 4);
   }
   if (c->weight == H3X_I8) {
     const size_t d = c->d_model, f = c->ffn_inner;
     const size_t most = 3 * d * d > 2 * f * d ? 3 * d * d : 2 * f * d;  // the largest matrix
-    w.w16 = base + off; off = align256(off + most * 2);
+    w.w16 = at(base, off); off = align256(off + most * 2);
   }
   w.bytes = off;
   return w;
@@ -393,13 +400,13 @@ StepWs step_layout(const h3x_block_cfg* c, const h3x_geom* g, uint8_t* base) {
   size_t off = align256(w.blk.bytes);
   const size_t es = elem_bytes(c->act);
   const int64_t n = geom_tokens(g);
-  w.x = base + off; off = align256(off + static_cast<size_t>(n) * c->d_model * es);
+  w.x = at(base, off); off = align256(off + static_cast<size_t>(n) * c->d_model * es);
   h3x_geom gm = *g;
   gm.merged = 1;
   const int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h * g->grid_w;
   const int64_t nm = nv / 2 + g->n_audio + g->n_text;
-  w.xm = base + off; off = align256(off + static_cast<size_t>(nm) * c->d_model * es);
-  w.rope_m = base + off; off += rope_bytes(c, &gm);
+  w.xm = at(base, off); off = align256(off + static_cast<size_t>(nm) * c->d_model * es);
+  w.rope_m = at(base, off); off += rope_bytes(c, &gm);
   w.bytes = off;
   return w;
 }
