@@ -108,6 +108,40 @@ def test_linear_f32out(B, wl, m):
     assert rel_l2(host(out), ref) < 2e-6
 
 
+# A gate/up projection with more tiles than the chip runs at once (3 x 192 = 576 tiles of
+# 256 x 256 for 700 rows and 2 x 24576 columns, a ragged last row of tiles): the XCD-ordered tile
+# walk over several rounds, against the plain product.
+WIDE = SMALL.replace(name="wide_bf16", ffn_inner=24576, seed_base=19)
+
+
+@pytest.mark.parametrize("weight", ["bf16", "i8"])
+def test_linear_many_tile_rounds(B, weight):
+    wl = WIDE.replace(weight=weight)
+    cfg = binding_cfg(wl)
+    m, d, f = 700, wl.d_model, wl.ffn_inner
+    rng = np.random.default_rng(23)
+    a = synth.storage_values(rng.standard_normal((m, d)).astype(np.float32), "bf16")
+    gu = synth.storage_values(rng.standard_normal((2 * f, d)).astype(np.float32) * np.float32(0.02), "bf16")
+    if weight == "i8":
+        w, s = B.pack_int8_weights(cfg, B.W_GATE_UP, to_dev(gu, "bf16"))
+        gu_r = quant.dequant(*quant.pack_int8(gu))
+    else:
+        w, s = B.pack_weights(cfg, B.W_GATE_UP, to_dev(gu, "bf16")), None
+        gu_r = gu.astype(np.float64)
+    ad = to_dev(a, "bf16")
+    out = host(B.linear_f32out(cfg, B.W_GATE_UP, ad, w, s))
+    perm = np.array([_src(B.W_GATE_UP, p, 2 * f) for p in range(2 * f)])
+    ref = a.astype(np.float64) @ gu_r[perm].T
+    assert rel_l2(out, ref) < 2e-6
+    h = host(B.linear_swiglu(cfg, ad, w, s))
+    a64 = a.astype(np.float64)
+    href = dit.silu(a64 @ gu_r[:f].T) * (a64 @ gu_r[f:].T)
+    assert rel_l2(h, href) < 5e-3
+    # Every row on its own, the ragged last tile row (rows 512..699) included.
+    den = np.linalg.norm(href, axis=1)
+    assert (np.linalg.norm(h - href, axis=1) / den).max() < 1e-2
+
+
 # ---------------------------------------------------------------- QKV + RoPE
 @pytest.mark.parametrize("wl,tol", [(SMALL, 5e-3), (SMALL_F32, 1e-5), (SMALL_I8, 5e-3)],
                          ids=["bf16", "f32", "i8"])

@@ -141,6 +141,28 @@ def test_linear_a8_matches_exact_integer_product(B, kind, m):
     assert not got[3].any()
 
 
+def test_linear_a8_many_tile_rounds(B):
+    """The gate/up projection at 700 rows and 2 x 24576 columns (576 tiles over several rounds
+    of the chip, a ragged last row of tiles), against the exact integer sums times the scales
+    (the sums, at most 127^2 x 512 in size, are exact in float64)."""
+    wl = SMALL_A8.replace(ffn_inner=24576, seed_base=20)
+    cfg = binding_cfg(wl)
+    m, d, f = 700, wl.d_model, wl.ffn_inner
+    rng = np.random.default_rng(44)
+    a = bf16_rne(rng.standard_normal((m, d)).astype(np.float32))
+    w = bf16_rne(rng.standard_normal((2 * f, d)).astype(np.float32) * np.float32(0.05))
+    qa, sa = B.quant_rows(to_dev(a, "bf16"))
+    qw, sw = B.pack_int8_weights(cfg, 2, to_dev(w, "bf16"))
+    got = B.linear_a8_f32out(cfg, 2, m, qa, sa, qw, sw).cpu().numpy().astype(np.float64)
+    qar, sar = quant.quant_act_rows(a)
+    qwr, swr = quant.pack_int8(w)
+    perm = np.array([_src(2, p, 2 * f) for p in range(2 * f)])
+    acc = qar.astype(np.float64) @ qwr[perm].astype(np.float64).T
+    ref = sar.astype(np.float64)[:, None] * swr[perm].astype(np.float64)[None, :] * acc
+    err = np.abs(got - ref)
+    assert np.all(err <= np.abs(ref) * 2.0 ** -22 + 1e-37), float((err / np.maximum(np.abs(ref), 1e-30)).max())
+
+
 def _a8_block_ref(x, w64, m64, og, nh, rows=None):
     return dit.block_forward(x, w64, m64, og, nh, rows=rows, act_quant=quant.w8a8_act("bf16"))
 

@@ -373,22 +373,27 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
-int attention_slots(int requested) {
-  const int cap = kAttnMaxPieceQueries / kAttnQueries;
-  if (requested > 0) return requested < cap ? requested : cap;
+int device_cu_count() {
   // The compute-unit count of each device, queried once per device (thread-safe).
   constexpr int kMaxDevices = 64;
   static std::once_flag once[kMaxDevices];
   static int cus[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return cap < 512 ? cap : 512;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
   std::call_once(once[dev], [dev] {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
     cus[dev] = n;
   });
+  return cus[dev];
+}
+
+int attention_slots(int requested) {
+  const int cap = kAttnMaxPieceQueries / kAttnQueries;
+  if (requested > 0) return requested < cap ? requested : cap;
   // One eight-wave workgroup per CU (two waves per SIMD).
-  return cus[dev] < cap ? cus[dev] : cap;
+  const int cus = device_cu_count();
+  return cus < cap ? cus : cap;
 }
 
 AttnPlan attention_plan(int64_t n_tokens, int n_heads, int slots) {

@@ -128,6 +128,7 @@ constexpr int kAttnMaxPieceQueries = 1 << 17;
 constexpr int kAttnQueries = 256;  // queries per workgroup of the bfloat16 attention (8 waves x 32)
 constexpr size_t attn_part_bytes(int bq) { return static_cast<size_t>(bq) * (128 * 4 + 2 * 4); }
 int attention_slots(int requested);  // 0 = what the current device runs at once
+int device_cu_count();               // compute units of the current device (queried once per device)
 AttnPlan attention_plan(int64_t n_tokens, int n_heads, int slots);
 size_t attention_ws_bytes(int act, int64_t n_tokens, int n_heads, int slots);
 hipError_t launch_attention(int act, int64_t n_tokens, int64_t n_pad, int n_heads, int head_dim,
