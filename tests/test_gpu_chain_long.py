@@ -45,16 +45,19 @@ def velocity_error_bound(n_blocks: int) -> float:
 RHO = 1.7e-3
 
 
-def drift_bounds(zs, vs, sig, n_blocks):
+def drift_bounds(zs, vs, sig, n_blocks, gains=None):
     """Bound on rel-L2(z_gpu_i, z_oracle_i) after each step i: the Euler update adds
     delta_j * v_j, so the state's error is at most the velocity error times
     sum_j |delta_j| |v_j| (all errors aligned), relative to |z_i|. The velocity error above
     counts the stream's stores only; the branches' own stores (y, q, k, v, o, y2, h) and the
-    kernels' float32 arithmetic are allowed as much again (factor 2)."""
+    kernels' float32 arithmetic are allowed as much again (factor 2). gains[j] scales step j's
+    velocity error: an extrapolated velocity v_a + w (v_a - v_b) carries up to 1 + 2|w| times
+    the error of a fresh one."""
     eps = velocity_error_bound(n_blocks)
     acc, out = 0.0, []
     for i, (z, v) in enumerate(zip(zs, vs)):
-        acc += abs(float(sig[i + 1]) - float(sig[i])) * np.linalg.norm(v)
+        g = 1.0 if gains is None else gains[i]
+        acc += abs(float(sig[i + 1]) - float(sig[i])) * np.linalg.norm(v) * g
         out.append(2.0 * eps * acc / np.linalg.norm(z))
     return out
 
@@ -103,6 +106,69 @@ def test_long_chain_no_restart(B, record, monkeypatch):
     # No row may stray: every state row within 3x the final bound.
     worst = row_rel_l2(z_gpu[-1], z_ref[-1]).max()
     record("long_chain final z worst row", worst, 3 * bounds[-1])
+    assert worst < 3 * bounds[-1]
+
+
+@pytest.mark.parametrize("variant", ["core4_tr10_34", "extrapolation"])
+def test_long_chain_variants_no_restart(B, record, variant):
+    """The same 45-block, 20-step schedule at d 256 with a sampler variant, end to end: core
+    reuse 4 over blocks 10..34 inside token reduction over the same blocks (reuse 1: the core's
+    kept change lives in the merged geometry, refreshed on 6 of the 20 steps), or whole reuse 2
+    with linear velocity extrapolation on the reused steps (siami.tw control table, rows
+    "核心復用" and "整體 denoiser 復用"; mobbang.com / jdon.com list of tested schedules)."""
+    wl = synth.TINY_LONG
+    core = None
+    if variant.startswith("core"):
+        wl = wl.replace(reuse=1)
+        core = (4, 10, 34)
+    extrap = variant == "extrapolation"
+    cfg, g, og = binding_cfg(wl), binding_geom(wl), oracle_geom(wl)
+    blocks64, packed = zip(*(packed_block(wl, b) for b in range(wl.n_blocks)))
+    arr = B.block_array(packed)
+    z0 = synth.initial_state(wl)
+    c = synth.storage_values(synth.text_rows(wl), "bf16")
+    zd = torch.from_numpy(z0.copy()).cuda()
+    cd = to_dev(c, "bf16")
+    vd = torch.zeros(wl.n_state, wl.d_model, dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(vd) if extrap else None
+    dd = torch.zeros(og.n_tokens, wl.d_model, dtype=torch.float32, device="cuda") if core else None
+    ws = B.alloc_workspace(B.step_workspace_bytes(cfg, g))
+    sig = sampler.sigma_grid(wl.n_steps)
+    fresh = [i for i in range(wl.n_steps) if sampler.is_fresh(i, wl.n_steps, wl.reuse)]
+    weights = []
+    for i in range(wl.n_steps):
+        past = [j for j in fresh if j < i]
+        w = 0.0
+        if extrap and i not in fresh and len(past) >= 2:
+            w = float(sampler.extrapolation_weight(sig[i], sig[past[-1]], sig[past[-2]]))
+            assert np.float32(B.extrapolation_weight(float(sig[i]), float(sig[past[-1]]), float(sig[past[-2]]))) == np.float32(w)
+        weights.append(w)
+    mods = [[synth.modulation(wl, i, b) for b in range(wl.n_blocks)] for i in range(wl.n_steps)]
+    z_gpu = []
+    for i in range(wl.n_steps):
+        B.denoise_step(cfg, g, i, wl.n_steps, wl.reuse, float(sig[i]), float(sig[i + 1]), arr,
+                       torch.from_numpy(np.stack(mods[i])).cuda(), zd, cd, vd, ws, wl.tr_first, wl.tr_last,
+                       v_prev=vp, extrap=weights[i], core_reuse=core[0] if core else 0,
+                       core_first=core[1] if core else 0, core_last=core[2] if core else 0, core_delta=dd)
+        z_gpu.append(zd.cpu().numpy().astype(np.float64))
+    z, v, v_prev, delta = z0.copy(), None, None, None
+    z_ref, v_ref = [], []
+    for i in range(wl.n_steps):
+        z, v, v_prev, d_new = sampler.denoise_step_full(
+            z, c, v, blocks64, mods[i], og, wl.n_heads, "bf16", i, wl.n_steps, wl.reuse, sig[i], sig[i + 1],
+            wl.tr_first, wl.tr_last, v_prev=v_prev, extrap=weights[i],
+            core=(core[0], core[1], core[2], delta) if core else None)
+        if core:
+            delta = d_new
+        z_ref.append(z.astype(np.float64))
+        v_ref.append(np.asarray(v, np.float64))
+    bounds = drift_bounds(z_ref, v_ref, sig, wl.n_blocks, gains=[1.0 + 2.0 * abs(w) for w in weights])
+    for i in range(wl.n_steps):
+        e = rel_l2(z_gpu[i], z_ref[i])
+        record(f"long_chain[{variant}] step {i} z vs oracle", e, bounds[i])
+        assert e < bounds[i], (i, e, bounds[i])
+    worst = row_rel_l2(z_gpu[-1], z_ref[-1]).max()
+    record(f"long_chain[{variant}] final z worst row", worst, 3 * bounds[-1])
     assert worst < 3 * bounds[-1]
 
 

@@ -194,6 +194,35 @@ def test_attention(B, wl, tol, n, sharp):
     assert rel_l2(host(o), ref) < tol
 
 
+@pytest.mark.parametrize("slots", [0, 1])
+def test_attention_needles_in_every_key_tile(B, record, slots):
+    """Each query's own key dominates its softmax (q_i = 3 k_j(i), logits of about 34 against a
+    spread of about 3): the keys j(i) run over every 64-key tile, the first and the last key of
+    each and both ends of the ragged last tile (363 = 5 x 64 + 43 keys), so a skipped, masked or
+    misplaced tile, or a wrong key order inside a tile, moves whole rows; every row is checked
+    on its own. slots 0: the device's plan (key pieces); 1: every item whole."""
+    wl = SMALL
+    cfg = binding_cfg(wl)
+    n, d = 363, wl.d_model
+    npad = B.pad_rows(n)
+    rng = np.random.default_rng(12)
+    kv = synth.storage_values(rng.standard_normal((n, d)).astype(np.float32), "bf16")
+    vv = synth.storage_values(rng.standard_normal((n, d)).astype(np.float32), "bf16")
+    needles = sorted({j for t in range(0, n, 64) for j in (t, t + 1, min(t + 63, n - 1))} | {n - 43, n - 2, n - 1})
+    j_of = np.array([needles[i % len(needles)] if i % 3 else (i * 7) % n for i in range(n)])
+    qv = synth.storage_values(3.0 * kv[j_of], "bf16")
+    qp, kp = np.zeros((npad, d), np.float32), np.zeros((npad, d), np.float32)
+    vtp = np.zeros((d, npad), np.float32)
+    qp[:n], kp[:n], vtp[:, :n] = qv, kv, vv.T
+    o = host(B.attention(cfg, n, to_dev(qp, "bf16"), to_dev(kp, "bf16"), to_dev(vtp, "bf16"), slots=slots))
+    ref = dit.attention(qv, kv, vv, wl.n_heads)
+    # The references are dominated by the needles' values (the pin that the test is sharp).
+    assert rel_l2(ref, vv[j_of]) < 0.3
+    rows = np.linalg.norm(o - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    record(f"attention_needles[slots={slots}] worst row", rows.max(), 1e-2)
+    assert rows.max() < 1e-2, int(rows.argmax())
+
+
 @pytest.mark.parametrize("slots", [16, 12, 5, 100, 0])
 def test_attention_work_split(B, record, slots):
     """The work plan for `slots` resident workgroups, for 1000 tokens and 4 heads (16 items of
