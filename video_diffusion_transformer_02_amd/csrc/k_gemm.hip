@@ -221,14 +221,19 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
       }
     }
   };
+  // The MFMAs of a slice walk the (m-block, n-block) grid in snake order, so that each one
+  // changes only one of its two operands from the one before (the matrix cores draw less power
+  // when fewer operand bits toggle; measured 0.3-1 % faster on the bf16 GEMMs).
   auto mma = [&](const Frags& f) {
     if constexpr (kA8) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int j = 0; j < NB; ++j) {
+          const int nb = (mb & 1) ? NB - 1 - j : j;
           acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, f.a[mb]),
                                                              __builtin_bit_cast(i32x4, f.b[nb]), acc[mb][nb], 0, 0, 0);
+        }
       return;
     }
     bf16x8 bv[NB];
@@ -240,8 +245,10 @@ __global__ __launch_bounds__(Layout<kWN>::kThreadsT, 1) void gemm_mfma_kernel(Ge
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int j = 0; j < NB; ++j) {
+        const int nb = (mb & 1) ? NB - 1 - j : j;
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a[mb]), bv[nb], acc[mb][nb], 0, 0, 0);
+      }
   };
   // Ping-pong schedule (eight waves, two per SIMD): waves 0-3 and 4-7 alternate between a
   // memory phase (stream a future K step into LDS, read this K step's fragments) and a
