@@ -10,6 +10,8 @@ own input to that block: K and V for every row, the rest for 64 sampled rows).
   to the checked step, which is then replayed block by block through h3x_dit_block_forward,
   h3x_token_merge and h3x_token_unmerge; the replay's velocity must equal h3x_denoise_step's bit
   for bit;
+* the 50-block, 4-step schedule at 6 x 30 x 54 + 256 + 512 tokens with int8 weights (W8A16),
+  checked at blocks 0, 24 and 49 of steps 0 and 3 against the oracle with the dequantised weights;
 * one W8A8 block at 6 x 30 x 54 + 256 + 512 tokens (jdon.com, "选配还是选速").
 """
 import numpy as np
@@ -161,6 +163,75 @@ def test_schedule_checkpoint_blocks(B, stack45, tr, step, record):
         _say(f"{name}: rel-L2 {e:.2e}, worst row {worst:.2e}, branch {eb:.2e} (bound {bb:.2e})")
         assert e < TOL and worst < ROW_FACTOR * TOL and eb < bb, (b, e, worst, eb, bb)
         del w64
+
+
+# ---------------------------------------------------------------- the 50-block int8-weight schedule
+INT8_CHECK_BLOCKS = (0, 24, 49)
+
+
+@pytest.mark.parametrize("step", [0, 3])
+def test_int8_schedule_checkpoint_blocks(B, step, record):
+    """The 50-block, 4-step schedule at 6 x 30 x 54 + 256 + 512 tokens (10488) with per-output-
+    channel int8 weights (W8A16): blocks 0, 24 and 49 of steps 0 and 3 against the oracle with
+    the dequantised weights, from the GPU's own block inputs (siami.tw, "2. 數據會說話": int8
+    weights for the 50-layer renders). The checked step is replayed block by block and its
+    velocity must equal h3x_denoise_step's bit for bit. The oracle's weights are the packed ones
+    exactly (dequantised), so the bfloat16 activation bar applies."""
+    wl = synth.INT8_50
+    cfg, g, og = binding_cfg(wl), binding_geom(wl), oracle_geom(wl)
+    seed0 = 19000
+    master = lambda b: {"qkv": _draw((3 * wl.d_model, wl.d_model), seed0 + 5 * b),
+                        "out": _draw((wl.d_model, wl.d_model), seed0 + 5 * b + 1),
+                        "gate": _draw((wl.ffn_inner, wl.d_model), seed0 + 5 * b + 2),
+                        "up": _draw((wl.ffn_inner, wl.d_model), seed0 + 5 * b + 3),
+                        "down": _draw((wl.d_model, wl.ffn_inner), seed0 + 5 * b + 4)}
+    packed = [B.pack_block(cfg, master(b)) for b in range(wl.n_blocks)]
+    arr = B.block_array(packed)
+    sig = sampler.sigma_grid(wl.n_steps)
+    mods = lambda i: np.stack([synth.modulation(wl, i, b) for b in range(wl.n_blocks)])
+    zd = torch.from_numpy(synth.initial_state(wl)).cuda()
+    cd = to_dev(synth.storage_values(synth.text_rows(wl), "bf16"), "bf16")
+    vd = torch.zeros(wl.n_state, wl.d_model, dtype=torch.bfloat16, device="cuda")
+    ws = B.alloc_workspace(B.step_workspace_bytes(cfg, g))
+    for i in range(step):
+        B.denoise_step(cfg, g, i, wl.n_steps, wl.reuse, float(sig[i]), float(sig[i + 1]), arr,
+                       torch.from_numpy(mods(i)).cuda(), zd, cd, vd, ws)
+    md = torch.from_numpy(mods(step)).cuda()
+    cur = torch.cat([zd.to(torch.bfloat16), cd], 0).contiguous()
+    bws = B.alloc_workspace(B.block_workspace_bytes(cfg, g))
+    seen = {}
+    for b in range(wl.n_blocks):
+        if b in INT8_CHECK_BLOCKS:
+            x_in = host(cur)
+        B.dit_block_forward(cfg, g, packed[b], md[b], cur, bws)
+        if b in INT8_CHECK_BLOCKS:
+            seen[b] = (x_in, host(cur))
+    v_replay = cur[:wl.n_state].clone()
+    B.denoise_step(cfg, g, step, wl.n_steps, wl.reuse, float(sig[step]), float(sig[step + 1]), arr, md,
+                   zd, cd, vd, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(vd.view(torch.int16), v_replay.view(torch.int16))
+    del ws, bws, packed, arr
+    torch.cuda.empty_cache()
+    _say(f"[int8 checkpoint] step={step}: replay matches h3x_denoise_step")
+    rows = synth.sample_rows(wl)
+    for b in INT8_CHECK_BLOCKS:
+        x_in, x_out = seen[b]
+        w64 = {}
+        for k, t in master(b).items():
+            q, sc = quant.pack_int8(t.float().cpu().numpy())
+            w64[k] = quant.dequant(q, sc)
+        m64 = synth.modulation(wl, step, b).astype(np.float64)
+        ref = dit.block_forward(x_in, w64, m64, og, wl.n_heads, rows=rows)
+        got = x_out[rows]
+        e, worst = rel_l2(got, ref), row_rel_l2(got, ref).max()
+        eb, bb = rel_l2(got - x_in[rows], ref - x_in[rows]), branch_bound(wl, x_in[rows], ref)
+        name = f"int8 checkpoint[step {step},block {b}]"
+        record(name, e, TOL)
+        record(name + " worst row", worst, ROW_FACTOR * TOL)
+        record(name + " branch", eb, bb)
+        _say(f"{name}: rel-L2 {e:.2e}, worst row {worst:.2e}, branch {eb:.2e} (bound {bb:.2e})")
+        assert e < TOL and worst < ROW_FACTOR * TOL and eb < bb, (b, e, worst, eb, bb)
 
 
 # ---------------------------------------------------------------- W8A8 at 6 x 30 x 54
