@@ -194,6 +194,43 @@ def test_attention(B, wl, tol, n, sharp):
     assert rel_l2(host(o), ref) < tol
 
 
+def test_attention_longest_sequence(B, record):
+    """The longest sequence whose bfloat16 K and V^T the attention kernel can address with 32-bit
+    buffer offsets at d = 6144 (48 heads x 128): N = 174592 tokens, N * d * 2 bytes just under
+    2^31. Checked on sampled query rows (the first and the last 32, and 64 drawn at random)
+    against the oracle over all N keys; inputs drawn on the GPU from a seeded generator."""
+    d, heads = 6144, 48
+    n = (2 ** 31 - 1) // (d * 2) // 256 * 256
+    assert n == 174592 and n * d * 2 < 2 ** 31
+    cfg = B.BlockCfg.make(d, heads, 128, 4 * d, "bf16", "bf16")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(174592)
+    draw = lambda scale: (torch.randn((n, d), generator=gen, device="cuda") * scale).to(torch.bfloat16)
+    q, k, v = draw(2.0), draw(1.0), draw(1.0)
+    vt = v.t().contiguous()
+    print(f"[longest] attention over {n} tokens", flush=True)
+    o = B.attention(cfg, n, q, k, vt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(n - 32, n), rng.integers(32, n - 32, 64)]))
+    ridx = torch.from_numpy(rows).cuda()
+    got = host(o.index_select(0, ridx))
+    qs = q.index_select(0, ridx).float().cpu().numpy()
+    del o, vt, q
+    kh = k.float().cpu().numpy()
+    del k
+    vh = v.float().cpu().numpy()
+    del v
+    torch.cuda.empty_cache()
+    ref = dit.attention(qs, kh, vh, heads)
+    e = rel_l2(got, ref)
+    worst = max(rel_l2(got[i], ref[i]) for i in range(len(rows)))
+    record("attention_longest_sequence", e, 5e-3)
+    record("attention_longest_sequence worst row", worst, 1e-2)
+    print(f"[longest] rel-L2 {e:.2e}, worst row {worst:.2e}", flush=True)
+    assert e < 5e-3 and worst < 1e-2
+
+
 @pytest.mark.parametrize("slots", [0, 1])
 def test_attention_needles_in_every_key_tile(B, record, slots):
     """Each query's own key dominates its softmax (q_i = 3 k_j(i), logits of about 34 against a
