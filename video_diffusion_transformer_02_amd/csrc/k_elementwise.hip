@@ -16,10 +16,10 @@ template <class E> struct Vec;
 template <> struct Vec<F32> { static constexpr int n = 4; };
 template <> struct Vec<BF16> { static constexpr int n = 8; };
 
-// Load / store n consecutive elements (16 bytes) as floats.
+// Load / store n consecutive elements (16 bytes) as floats; unpack16 is load16 on a chunk
+// already in registers.
 template <class E>
-__device__ __forceinline__ void load16(const typename E::T* p, float* out) {
-  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void unpack16(const uint4 raw, float* out) {
   if constexpr (sizeof(typename E::T) == 4) {
     out[0] = __uint_as_float(raw.x); out[1] = __uint_as_float(raw.y);
     out[2] = __uint_as_float(raw.z); out[3] = __uint_as_float(raw.w);
@@ -31,6 +31,10 @@ __device__ __forceinline__ void load16(const typename E::T* p, float* out) {
       out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+}
+template <class E>
+__device__ __forceinline__ void load16(const typename E::T* p, float* out) {
+  unpack16<E>(*reinterpret_cast<const uint4*>(p), out);
 }
 template <class E>
 __device__ __forceinline__ void store16(typename E::T* p, const float* v) {
@@ -97,9 +101,11 @@ __global__ __launch_bounds__(kThreads) void norm_mod_kernel(const typename E::T*
   }
 }
 
-// kRows rows per workgroup with the rows held in registers (each row read once) and shift /
-// scale loaded once for all kRows rows; kChunks 16-byte chunks per thread and row cover
-// d <= kChunks * 256 * V. Same arithmetic, in the same order, as norm_mod_kernel.
+// kRows rows per workgroup with the rows held in registers as loaded (each row read once; 16
+// bytes per chunk, so bfloat16 rows take half the registers of float32 values and more
+// workgroups stay resident) and shift / scale loaded once for all kRows rows; kChunks 16-byte
+// chunks per thread and row cover d <= kChunks * 256 * V. Same arithmetic, in the same order,
+// as norm_mod_kernel.
 template <class E, int kChunks, int kRows>
 __global__ __launch_bounds__(kThreads) void norm_rows_kernel(const typename E::T* __restrict__ x,
                                                              const float* __restrict__ shift,
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(const typename E::T
   constexpr int V = Vec<E>::n;
   __shared__ float part[kRows][kThreads / 64];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRows;
-  float v[kRows][kChunks][V];
+  uint4 raw[kRows][kChunks];
   float ss[kRows];
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
@@ -119,10 +125,13 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(const typename E::T
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int i = (c * kThreads + threadIdx.x) * V;
+      raw[r][c] = make_uint4(0u, 0u, 0u, 0u);
       if (row < n_rows && i < d) {
-        load16<E>(x + row * d + i, v[r][c]);
+        raw[r][c] = *reinterpret_cast<const uint4*>(x + row * d + i);
+        float v[V];
+        unpack16<E>(raw[r][c], v);
 #pragma unroll
-        for (int j = 0; j < V; ++j) ss[r] = fmaf(v[r][c][j], v[r][c][j], ss[r]);
+        for (int j = 0; j < V; ++j) ss[r] = fmaf(v[j], v[j], ss[r]);
       }
     }
   }
@@ -156,9 +165,10 @@ __global__ __launch_bounds__(kThreads) void norm_rows_kernel(const typename E::T
     for (int r = 0; r < kRows; ++r) {
       const int64_t row = r0 + r;
       if (row >= n_rows) continue;
-      float o[V];
+      float v[V], o[V];
+      unpack16<E>(raw[r][c], v);
 #pragma unroll
-      for (int j = 0; j < V; ++j) o[j] = fmaf(v[r][c][j] * rs[r], sc[j], sh[j]);
+      for (int j = 0; j < V; ++j) o[j] = fmaf(v[j] * rs[r], sc[j], sh[j]);
       if (out_tiled)  // bf16 only: 256-row x 32-column slabs (see slab_offset)
         store16<E>(reinterpret_cast<typename E::T*>(reinterpret_cast<uint8_t*>(y) + slab_offset(row, i, d)), o);
       else
@@ -221,7 +231,9 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const uint16_t* __
   __shared__ float part[kRows][kThreads / 64];
   __shared__ float pmax[kRows][kThreads / 64];
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRows;
-  float v[kRows][kChunks][V];
+  // Each chunk stays in registers as its 8 bfloat16 values: first the input, then the
+  // normalised values rounded to bfloat16 (exactly what the codes are formed from).
+  uint4 raw[kRows][kChunks];
   float ss[kRows];
 #pragma unroll
   for (int r = 0; r < kRows; ++r) {
@@ -230,13 +242,13 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const uint16_t* __
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int i = (c * kThreads + threadIdx.x) * V;
+      raw[r][c] = make_uint4(0u, 0u, 0u, 0u);
       if (row < n_rows && i < d) {
-        load16<BF16>(x + row * d + i, v[r][c]);
+        raw[r][c] = *reinterpret_cast<const uint4*>(x + row * d + i);
+        float v[V];
+        unpack16<BF16>(raw[r][c], v);
 #pragma unroll
-        for (int j = 0; j < V; ++j) ss[r] = fmaf(v[r][c][j], v[r][c][j], ss[r]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < V; ++j) v[r][c][j] = 0.f;
+        for (int j = 0; j < V; ++j) ss[r] = fmaf(v[j], v[j], ss[r]);
       }
     }
   }
@@ -268,13 +280,18 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const uint16_t* __
       sh[4 * j] = b.x; sh[4 * j + 1] = b.y; sh[4 * j + 2] = b.z; sh[4 * j + 3] = b.w;
     }
 #pragma unroll
-    for (int r = 0; r < kRows; ++r)
+    for (int r = 0; r < kRows; ++r) {
+      float v[V];
+      unpack16<BF16>(raw[r][c], v);
+      uint32_t bits[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) {
-        const float o = bf16_bits_to_f32(f32_to_bf16_bits(fmaf(v[r][c][j] * rs[r], sc[j], sh[j])));
-        v[r][c][j] = o;
-        amax[r] = fmaxf(amax[r], fabsf(o));
+        bits[j] = f32_to_bf16_bits(fmaf(v[j] * rs[r], sc[j], sh[j]));
+        amax[r] = fmaxf(amax[r], fabsf(bf16_bits_to_f32(bits[j])));
       }
+      raw[r][c] = make_uint4(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16),
+                             bits[4] | (bits[5] << 16), bits[6] | (bits[7] << 16));
+    }
   }
   block_max_rows<kRows>(amax, pmax);
 #pragma unroll
@@ -287,7 +304,9 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const uint16_t* __
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int i = (c * kThreads + threadIdx.x) * V;
-      if (i < d) *reinterpret_cast<uint2*>(q + slab_offset_q8(row, i, d)) = quant8(v[r][c], inv);
+      float v[V];
+      unpack16<BF16>(raw[r][c], v);
+      if (i < d) *reinterpret_cast<uint2*>(q + slab_offset_q8(row, i, d)) = quant8(v, inv);
     }
   }
 }
