@@ -87,6 +87,24 @@ def test_norm_mod(B, wl, tol):
     assert rel_l2(host(y), ref) < tol
 
 
+@pytest.mark.parametrize("act,d", [("bf16", 256), ("bf16", 2304), ("bf16", 4096), ("bf16", 8192),
+                                   ("bf16", 10240), ("f32", 256), ("f32", 1536), ("f32", 4096)])
+def test_norm_mod_every_width(B, act, d):
+    """Every register-resident width of the four-row kernel (one to four 16-byte chunks per
+    thread and row) and the one-row kernel beyond it, with 13 rows (the last workgroup of four
+    rows ragged): every row within the bar of the oracle's."""
+    wl = SMALL.replace(d_model=d, n_heads=d // 128, act=act, weight=act)
+    cfg = binding_cfg(wl)
+    rng = np.random.default_rng(d)
+    x = synth.storage_values(rng.standard_normal((13, d)).astype(np.float32) * 2.0, act)
+    x[5] = 0.0
+    m = (rng.standard_normal((2, d)) * 0.3).astype(np.float32)
+    y = host(B.norm_mod(cfg, to_dev(x, act), torch.from_numpy(m[0]).cuda(), torch.from_numpy(m[1]).cuda()))
+    ref = dit.rms_norm_mod(x, m[0], m[1])
+    rows = np.linalg.norm(y - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert rows.max() < (5e-3 if act == "bf16" else 1e-6), (int(rows.argmax()), rows.max())
+
+
 # ---------------------------------------------------------------- contraction alone
 @pytest.mark.parametrize("wl", [SMALL, SMALL_I8, SMALL_F32], ids=lambda w: w.name)
 @pytest.mark.parametrize("m", [1, 255, 363, 700])
