@@ -52,16 +52,24 @@ class Timed {
     if (!g_prof_on) return;
     start_ = take_event();
     stop_ = take_event();
-    if (start_ && stop_) hipEventRecord(start_, s_);
+    if (start_ && stop_ && hipEventRecord(start_, s_) == hipSuccess) return;
+    give_back();  // no timing for this launch
   }
   ~Timed() {
     if (!start_ || !stop_) return;
-    hipEventRecord(stop_, s_);
+    const bool ok = hipEventRecord(stop_, s_) == hipSuccess;
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    g_prof_recs.push_back({name_, start_, stop_});
+    if (ok) g_prof_recs.push_back({name_, start_, stop_});
+    else give_back();
   }
 
  private:
+  // Returns the events to the pool (g_prof_mu held).
+  void give_back() {
+    if (start_) g_event_pool.push_back(start_);
+    if (stop_) g_event_pool.push_back(stop_);
+    start_ = stop_ = nullptr;
+  }
   const char* name_;
   hipStream_t s_;
   hipEvent_t start_ = nullptr, stop_ = nullptr;

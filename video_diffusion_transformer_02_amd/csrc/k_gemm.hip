@@ -52,11 +52,6 @@ __device__ __forceinline__ float rope_apply(float v, float p, float2 cs, bool ev
   return even ? fmaf(v, cs.x, -p * cs.y) : fmaf(p, cs.y, v * cs.x);
 }
 
-__device__ __forceinline__ float dpp_swap_adjacent(float v) {
-  // quad_perm [1, 0, 3, 2]: each lane receives its neighbour's value (lane ^ 1).
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-}
-
 // ---------------------------------------------------------------- MFMA kernel
 template <bool kInt8>
 struct Smem {
