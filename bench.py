@@ -291,10 +291,25 @@ def cpu_baseline(args, state):
     dt = time.perf_counter() - t0
     log(f"[bench] oracle sample: {reps} x ({r} query rows, {flops / 1e12:.3f} TFLOP) in {dt:.1f} s on {cores} threads"
         f" ({host})")
-    return {"value": round(reps * flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    # The schedules' work at the sample's rate (extrapolated, not timed): one block, one fresh
+    # step of the 45-block schedule without and with token reduction over blocks 10..34 (3840
+    # tokens when merged), one step of the 50-block schedule at 6 x 30 x 54 (10488 tokens).
+    rate = reps * flops / dt
+    nm = w.frames * w.grid_h * w.grid_w // 2 + w.n_audio + w.n_text
+    n4 = w.frames * 30 * 54 + w.n_audio + w.n_text
+    bf = block_flops(n, d, f)
+    extrapolated = {
+        "block_ms": round(bf / rate * 1e3, 1),
+        "denoise_45blk_fresh_step_ms": round(45 * bf / rate * 1e3, 1),
+        "denoise_45blk_tr10_34_fresh_step_ms": round((20 * bf + 25 * block_flops(nm, d, f)) / rate * 1e3, 1),
+        "int8w_50blk_6x30x54_step_ms": round(50 * block_flops(n4, d, f) / rate * 1e3, 1),
+        "how": "algorithmic FLOPs of the configuration / the sample's measured FLOP rate",
+    }
+    return {"value": round(rate / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"one block at the same shape: K/V of all {n} rows plus {r} of {n} query rows "
                       f"({flops / 1e12:.3f} TFLOP per pass), {reps} passes in {dt:.1f} s",
-            "threads": "cores = BLAS threads the oracle ran on", "host": host}
+            "threads": "cores = BLAS threads the oracle ran on", "host": host,
+            "extrapolated": extrapolated}
 
 
 def host_cpu():
