@@ -20,9 +20,10 @@ def B():
     return binding
 
 
-@pytest.mark.parametrize("weight", ["bf16", "i8a8"])
+@pytest.mark.parametrize("weight", ["bf16", "i8", "i8a8", "f32"])
 def test_noalloc_matches_workspace_entry_point(B, weight):
-    big = SMALL.replace(name=f"noalloc_big_{weight}", weight=weight, seed_base=61)
+    act = "f32" if weight == "f32" else "bf16"
+    big = SMALL.replace(name=f"noalloc_big_{weight}", weight=weight, act=act, seed_base=61)
     small = big.replace(name=f"noalloc_small_{weight}", frames=1, grid_h=4, grid_w=6, n_audio=5, n_text=7,
                         seed_base=62)
     for wl in (big, small):
@@ -30,14 +31,14 @@ def test_noalloc_matches_workspace_entry_point(B, weight):
         assert B.block_workspace_bytes(cfg, g) <= B.NOALLOC_SCRATCH_BYTES
         _, pb = packed_block(wl, 0)
         _, mdev = modulation(wl, 0, 0)
-        x = synth.storage_values(synth.normal(wl.seed_base, 3, (og.n_tokens, wl.d_model)), "bf16")
-        xa, xb = to_dev(x, "bf16"), to_dev(x, "bf16")
+        x = synth.storage_values(synth.normal(wl.seed_base, 3, (og.n_tokens, wl.d_model)), act)
+        xa, xb = to_dev(x, act), to_dev(x, act)
         ws = B.alloc_workspace(B.block_workspace_bytes(cfg, g))
         B.dit_block_forward(cfg, g, pb, mdev, xa, ws)
         B.dit_block_forward_noalloc(cfg, g, pb, mdev, xb)
         torch.cuda.synchronize()
-        assert torch.equal(xa.view(torch.int16), xb.view(torch.int16)), wl.name
-        assert not torch.equal(xb.view(torch.int16), to_dev(x, "bf16").view(torch.int16))
+        assert torch.equal(xa.view(torch.uint8), xb.view(torch.uint8)), wl.name
+        assert not torch.equal(xb.view(torch.uint8), to_dev(x, act).view(torch.uint8))
 
 
 def test_noalloc_refuses_a_block_beyond_the_scratch(B):
