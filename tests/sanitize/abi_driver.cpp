@@ -44,6 +44,8 @@ int main() {
   EXPECT(h3x_geom_tokens(&g6912) == 6912);
   h3x_geom bad = {1, 3, 5, 0, 0, 1};
   EXPECT(h3x_geom_tokens(&bad) == -1);
+  h3x_geom huge = {2147483647, 2147483647, 2147483647, 0, 0, 0};  // product beyond 64 bits
+  EXPECT(h3x_geom_tokens(&huge) == -1);
   EXPECT(h3x_attention_workspace_bytes(&big, 6912, 0) == 0 || h3x_attention_workspace_bytes(&big, 6912, 256) > 0);
   EXPECT(h3x_rope_table_bytes(&big, &g6912) > 0);
 

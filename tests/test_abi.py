@@ -113,6 +113,15 @@ def test_geometry_validation(B):
     assert L.h3x_geom_tokens(ctypes.byref(B.Geom(1, 3, 5, 0, 0, 1))) == -1  # odd width merged
     assert L.h3x_geom_tokens(ctypes.byref(B.Geom(0, 0, 0, 0, 0, 0))) == -1
     assert L.h3x_geom_tokens(ctypes.byref(B.Geom(-1, 2, 2, 0, 0, 0))) == -1
+    # Sizes whose product would overflow 64 bits, a grid extent above 2^20 (the RoPE table's
+    # int32 indices) or more than 2^26 tokens are refused.
+    big = 2 ** 31 - 1
+    assert L.h3x_geom_tokens(ctypes.byref(B.Geom(big, big, big, 0, 0, 0))) == -1
+    assert L.h3x_geom_tokens(ctypes.byref(B.Geom(1, 1, (1 << 20) + 2, 0, 0, 0))) == -1
+    assert L.h3x_geom_tokens(ctypes.byref(B.Geom(1, 1, 1 << 20, 0, 0, 0))) == 1 << 20
+    assert L.h3x_geom_tokens(ctypes.byref(B.Geom(1 << 13, 1 << 13, 2, 0, 0, 0))) == -1
+    assert L.h3x_geom_tokens(ctypes.byref(B.Geom(1 << 13, 1 << 13, 1, 0, 0, 0))) == 1 << 26
+    assert L.h3x_geom_tokens(ctypes.byref(B.Geom(0, 0, 0, big, big, 0))) == -1
 
 
 def test_block_forward_rejects_before_launch(B):
