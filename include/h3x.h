@@ -73,7 +73,9 @@ typedef enum {
  *   act F32  + weight F32  : head_dim 64 or 128, d_model % 64 == 0, ffn_inner % 64 == 0;
  *   act BF16 + weight BF16 or I8 : head_dim 128, d_model % 256 == 0, ffn_inner % 128 == 0;
  *   act BF16 + weight I8A8       : as BF16, and d_model <= 8192, ffn_inner <= 32768.
- * d_model must equal n_heads * head_dim. norm_eps > 0 (1e-6), rope_theta > 1 (10000). */
+ * d_model must equal n_heads * head_dim, d_model <= 65536 and ffn_inner <= 262144 (one GEMM
+ * operand panel of 256 rows is addressed with 32-bit offsets). norm_eps > 0 (1e-6),
+ * rope_theta > 1 (10000). Row and token counts of every call are at most 2^26. */
 typedef struct {
   int32_t d_model, n_heads, head_dim, ffn_inner;
   int32_t act;    /* h3x_dtype of activations: H3X_F32 or H3X_BF16 */

@@ -94,6 +94,8 @@ def test_cfg_validation(B):
         (dict(norm_eps=0.0), 1), (dict(rope_theta=1.0), 1), (dict(weight=7), 1),
         (dict(act="f32", weight="i8a8"), 2),
         (dict(weight="i8a8", d_model=8448, n_heads=66), 2), (dict(weight="i8a8", ffn_inner=32896), 2),
+        # Beyond the widths whose operand panels fit 32-bit buffer offsets.
+        (dict(d_model=65536 + 256, n_heads=514), 2), (dict(ffn_inner=262144 + 128), 2),
     ]
     for kw, status in bad:
         c = _cfg(B, **kw)
@@ -333,6 +335,8 @@ def test_zero_row_calls_enqueue_nothing(B):
     assert L.h3x_linear_a8_f32out(ctypes.byref(ca), 1, 0, None, None, None, None, None, None) == 0
     # The row count is still range-checked, and the other arguments still validated.
     assert L.h3x_norm_mod(ctypes.byref(c), -1, None, None, None, None, None) == 1
+    assert L.h3x_norm_mod(ctypes.byref(c), (1 << 26) + 1, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.h3x_euler(ctypes.byref(c), 1 << 40, FAKE, FAKE, 1.0, 0.5, None, None) == 1
     assert L.h3x_quant_rows(0, 100, None, None, None, None) == 1
     assert L.h3x_linear_f32out(ctypes.byref(c), 7, 0, None, None, None, None, None) == 1
 

@@ -101,6 +101,9 @@ h3x_status check_cfg(const h3x_block_cfg* c) {
     return fail(H3X_EINVAL, "cfg: sizes must be positive");
   if (static_cast<int64_t>(c->n_heads) * c->head_dim != c->d_model)
     return fail(H3X_EINVAL, "cfg: d_model != n_heads * head_dim");
+  // The GEMMs address one operand panel (256 rows x K) with 32-bit buffer offsets.
+  if (c->d_model > 65536 || c->ffn_inner > 262144)
+    return fail(H3X_ENOTSUP, "cfg: d_model <= 65536 and ffn_inner <= 262144 supported");
   if (!(c->norm_eps > 0.f) || !isfinite(c->norm_eps)) return fail(H3X_EINVAL, "cfg: norm_eps must be > 0");
   if (!(c->rope_theta > 1.f) || !isfinite(c->rope_theta)) return fail(H3X_EINVAL, "cfg: rope_theta must be > 1");
   if (c->act != H3X_F32 && c->act != H3X_BF16) return fail(H3X_EINVAL, "cfg: act must be F32 or BF16");
@@ -776,7 +779,7 @@ h3x_status h3x_norm_mod(const h3x_block_cfg* c, int64_t n_rows, const void* x, c
                         const float* scale, void* y, void* stream) {
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
-  if (n_rows < 0) return fail(H3X_EINVAL, "norm_mod: n_rows < 0");
+  if (n_rows < 0 || n_rows > (int64_t(1) << 26)) return fail(H3X_EINVAL, "norm_mod: bad n_rows");
   if (n_rows == 0) return H3X_OK;
   if (!x || !shift || !scale || !y || !aligned16(x) || !aligned16(y) || !aligned16(shift) || !aligned16(scale))
     return fail(H3X_EINVAL, "norm_mod: NULL or misaligned pointer");
@@ -964,7 +967,7 @@ h3x_status h3x_euler(const h3x_block_cfg* c, int64_t n_rows, float* z, const voi
                      float sigma_next, void* v_copy, void* stream) {
   h3x_status st = check_cfg(c);
   if (st != H3X_OK) return st;
-  if (n_rows < 0) return fail(H3X_EINVAL, "euler: n_rows < 0");
+  if (n_rows < 0 || n_rows > (int64_t(1) << 26)) return fail(H3X_EINVAL, "euler: bad n_rows");
   if (n_rows == 0) return H3X_OK;
   if (!isfinite(sigma) || !isfinite(sigma_next)) return fail(H3X_EINVAL, "euler: non-finite sigma");
   if (!z || !v || !aligned16(z) || !aligned16(v) || (v_copy && !aligned16(v_copy)))
