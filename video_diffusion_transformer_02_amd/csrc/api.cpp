@@ -132,16 +132,13 @@ h3x_status check_geom(const h3x_geom* g) {
     return fail(H3X_EINVAL, "geom: negative size");
   if (g->merged != 0 && g->merged != 1) return fail(H3X_EINVAL, "geom: merged must be 0 or 1");
   if (g->merged && (g->grid_w % 2)) return fail(H3X_EINVAL, "geom: merged geometry needs an even grid_w");
-  // Bounded step by step, so that the product cannot overflow: each factor and each partial
-  // product stays at most 2^26 before the next multiplication. Each grid extent is also at
-  // most 2^20, which keeps the RoPE table's int32 entry indices in range.
+  // Each grid extent is at most 2^20 (which keeps the RoPE table's int32 entry indices in
+  // range), so their product stays below 2^60 and is formed without overflow.
   const int64_t lim = int64_t(1) << 26, grid_lim = int64_t(1) << 20;
   if (g->frames > grid_lim || g->grid_h > grid_lim || g->grid_w > grid_lim)
     return fail(H3X_EINVAL, "geom: a grid extent above 2^20");
   if (g->n_audio > lim || g->n_text > lim) return fail(H3X_EINVAL, "geom: too many tokens");
-  int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h;
-  if (nv > lim) return fail(H3X_EINVAL, "geom: too many tokens");
-  nv *= g->grid_w;
+  const int64_t nv = static_cast<int64_t>(g->frames) * g->grid_h * g->grid_w;
   const int64_t n = (g->merged ? nv / 2 : nv) + g->n_audio + g->n_text;
   if (n <= 0) return fail(H3X_EINVAL, "geom: no tokens");
   if (n > lim) return fail(H3X_EINVAL, "geom: too many tokens");
