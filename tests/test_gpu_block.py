@@ -188,7 +188,7 @@ def test_denoise_chain_reuse(B, wl, record):
         assert e_dz < 3 * _tol(wl), (i, e_dz)
 
 
-@pytest.mark.parametrize("wl", [SMALL, SMALL_F32], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [SMALL, SMALL_F32, SMALL_I8], ids=lambda w: w.name)
 def test_denoise_chain_token_reduction(B, wl, record):
     errs = _chain(B, wl, 4, 3, 1, tr=(1, 2))
     record(f"denoise_chain_tr[{wl.name}] max dz", max(e[1] for e in errs), 3 * _tol(wl))

@@ -7,7 +7,7 @@ import torch
 import synth
 from oracle import sampler, tokred
 from _util import binding_cfg, binding_geom, oracle_geom, packed_block, rel_l2, to_dev
-from test_gpu_kernels import SMALL
+from test_gpu_kernels import SMALL, SMALL_I8
 
 pytestmark = pytest.mark.gpu
 
@@ -110,7 +110,7 @@ def test_fresh_step_moves_velocity_to_v_prev(B):
 
 
 @pytest.mark.parametrize("tr", [(-1, -1), (0, 3), (1, 2)], ids=["no_tr", "tr0_3", "tr1_2"])
-@pytest.mark.parametrize("wl", [synth.TINY, SMALL], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [synth.TINY, SMALL, SMALL_I8], ids=lambda w: w.name)
 def test_core_reuse_chain(B, wl, tr, record):
     """Four blocks, core = blocks 1..2 refreshed every 2nd step: steps 0 (core fresh), 1 (core
     reused), 2 (the last step: fresh), each checked against the oracle from the oracle's state.
