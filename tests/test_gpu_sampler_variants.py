@@ -42,7 +42,8 @@ def _mods(wl, step, n_blocks, zero_gates=()):
     return mods
 
 
-@pytest.mark.parametrize("wl,cf,cl", [(synth.TINY, 1, 0), (SMALL, 1, 1)], ids=["tiny_f32", "small_bf16"])
+@pytest.mark.parametrize("wl,cf,cl", [(synth.TINY, 1, 0), (SMALL, 1, 1), (SMALL_I8, 0, 1)],
+                         ids=["tiny_f32", "small_bf16", "small_i8_last_frame"])
 def test_fixed_condition_rows(B, wl, cf, cl, record):
     wl, cfg, g, og, b64, arr, c, ws = _setup(B, wl, 2)
     z = synth.initial_state(wl)
