@@ -5,13 +5,19 @@ import pytest
 import torch
 
 import synth
-from oracle import sampler, tokred
+from oracle import quant, sampler, tokred
 from _util import binding_cfg, binding_geom, oracle_geom, packed_block, rel_l2, to_dev
 from test_gpu_kernels import SMALL, SMALL_I8
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 1e-2}
+# W8A8 (per-row int8 activations): the block bar of the W8A8 block tests.
+SMALL_A8 = SMALL.replace(name="small_i8a8", weight="i8a8", seed_base=14)
+
+
+def _tol(wl):
+    return 2e-2 if wl.weight == "i8a8" else TOL[wl.act]
 
 
 @pytest.fixture(scope="module")
@@ -42,8 +48,8 @@ def _mods(wl, step, n_blocks, zero_gates=()):
     return mods
 
 
-@pytest.mark.parametrize("wl,cf,cl", [(synth.TINY, 1, 0), (SMALL, 1, 1), (SMALL_I8, 0, 1)],
-                         ids=["tiny_f32", "small_bf16", "small_i8_last_frame"])
+@pytest.mark.parametrize("wl,cf,cl", [(synth.TINY, 1, 0), (SMALL, 1, 1), (SMALL_I8, 0, 1), (SMALL_A8, 1, 1)],
+                         ids=["tiny_f32", "small_bf16", "small_i8_last_frame", "small_i8a8"])
 def test_fixed_condition_rows(B, wl, cf, cl, record):
     wl, cfg, g, og, b64, arr, c, ws = _setup(B, wl, 2)
     z = synth.initial_state(wl)
@@ -63,11 +69,12 @@ def test_fixed_condition_rows(B, wl, cf, cl, record):
     np.testing.assert_array_equal(zc[fixed].view(np.uint32), z[fixed].view(np.uint32))
     np.testing.assert_array_equal(zc[~fixed].view(np.uint32), z0[~fixed].view(np.uint32))
     np.testing.assert_array_equal(vc, v0)  # the DiT saw the same rows
+    aq = quant.w8a8_act("bf16") if wl.weight == "i8a8" else None
     ref = sampler.denoise_step_full(z, c, None, b64, mods, og, wl.n_heads, wl.act, 0, 4, 1, 1.0, 0.75,
-                                    cond_first=cf, cond_last=cl)[0]
+                                    cond_first=cf, cond_last=cl, act_quant=aq)[0]
     err = rel_l2(zc - z, ref.astype(np.float64) - z)
-    record(f"cond_rows[{wl.name}] step change", err, 3 * TOL[wl.act])
-    assert err < 3 * TOL[wl.act]
+    record(f"cond_rows[{wl.name}] step change", err, 3 * _tol(wl))
+    assert err < 3 * _tol(wl)
     # A reused step holds them too; the others take exactly the oracle's update.
     v = synth.storage_values(np.random.default_rng(3).standard_normal(z.shape).astype(np.float32), wl.act)
     zd = torch.from_numpy(z.copy()).cuda()
@@ -111,7 +118,7 @@ def test_fresh_step_moves_velocity_to_v_prev(B):
 
 
 @pytest.mark.parametrize("tr", [(-1, -1), (0, 3), (1, 2)], ids=["no_tr", "tr0_3", "tr1_2"])
-@pytest.mark.parametrize("wl", [synth.TINY, SMALL, SMALL_I8], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [synth.TINY, SMALL, SMALL_I8, SMALL_A8], ids=lambda w: w.name)
 def test_core_reuse_chain(B, wl, tr, record):
     """Four blocks, core = blocks 1..2 refreshed every 2nd step: steps 0 (core fresh), 1 (core
     reused), 2 (the last step: fresh), each checked against the oracle from the oracle's state.
@@ -127,6 +134,8 @@ def test_core_reuse_chain(B, wl, tr, record):
     dd = torch.zeros(og.n_tokens, wl.d_model, dtype=torch.float32, device="cuda")
     cdev = to_dev(c, wl.act)
     v, delta = None, None
+    tol = _tol(wl)
+    aq = quant.w8a8_act("bf16") if wl.weight == "i8a8" else None
     for i in range(n_steps):
         mods = _mods(wl, i, 4)
         B.denoise_step(cfg, g, i, n_steps, 1, float(sig[i]), float(sig[i + 1]), arr,
@@ -135,11 +144,11 @@ def test_core_reuse_chain(B, wl, tr, record):
         torch.cuda.synchronize()
         z_next, v, _, delta = sampler.denoise_step_full(z, c, v, b64, mods, og, wl.n_heads, wl.act, i, n_steps, 1,
                                                         sig[i], sig[i + 1], tr_first=tr[0], tr_last=tr[1],
-                                                        core=(k, 1, 2, delta))
+                                                        core=(k, 1, 2, delta), act_quant=aq)
         zg = zd.cpu().numpy().astype(np.float64)
         e = rel_l2(zg - z, z_next.astype(np.float64) - z)
-        record(f"core_reuse[{wl.name},tr={tr}] step {i} change", e, 3 * TOL[wl.act])
-        assert e < 3 * TOL[wl.act], (i, e)
+        record(f"core_reuse[{wl.name},tr={tr}] step {i} change", e, 3 * tol)
+        assert e < 3 * tol, (i, e)
         if i == 0:
             # The kept change is a difference of two stored residual streams: besides 3x the
             # block tolerance it carries their two storage roundings (RMS 2^-9/sqrt(3) of |x|
@@ -149,7 +158,7 @@ def test_core_reuse_chain(B, wl, tr, record):
             if tr[0] >= 0:
                 x0 = tokred.merge(x0, og, wl.act)
             assert delta.shape == (n_keep, wl.d_model)
-            bound = 3 * TOL[wl.act] + 2 * unit / np.sqrt(3) * np.linalg.norm(x0) / np.linalg.norm(delta) * 1.5
+            bound = 3 * tol + 2 * unit / np.sqrt(3) * np.linalg.norm(x0) / np.linalg.norm(delta) * 1.5
             ed = rel_l2(dd.cpu().numpy()[:n_keep], delta)
             record(f"core_reuse[{wl.name},tr={tr}] delta", ed, bound)
             assert ed < bound
