@@ -2,8 +2,9 @@
  * h3x_kernels.h -- kernel-level entry points of libh3x: one step of the block or the sampler
  * per call, for per-kernel parity tests and per-kernel timing. Same conventions as h3x.h
  * (device pointers named "dev", caller-owned buffers, asynchronous on `stream`, validation
- * before any launch, status codes, no allocation). A call with zero rows (n_rows, m) is valid,
- * enqueues nothing and does not look at its data pointers (they may be NULL).
+ * before any launch, status codes, no allocation). Row and token counts (n_rows, m, n_tokens)
+ * are at most 2^26 (else H3X_EINVAL). A call with zero rows (n_rows, m) is valid, enqueues
+ * nothing and does not look at its data pointers (they may be NULL).
  *
  * Internal attention layouts used by these entry points, for a sequence of N tokens and
  * Npad = N rounded up to a multiple of 256:
